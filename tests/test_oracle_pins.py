@@ -1,0 +1,335 @@
+"""Pins of the float64 oracle against things other than itself.
+
+* brute force in pure Python (math.fsum, tokens dealt round-robin) on tiny inputs;
+* a library special case: torch float64 scaled_dot_product_attention with an
+  explicit boolean mask, and torch.logsumexp for the LSE;
+* closed forms (one token, equal keys, zero query, two tokens);
+* invariants: split-then-merge equals unsplit for many (S, I); empty shards
+  change nothing; physical block order does not matter;
+* planted mistakes: each plausible oracle bug below is caught by one of these.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import mla_oracle
+from tests import _brute
+from workloads import build, bf16_rne_bits
+
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+def _tiny(seed, B=2, R=3, H=2, lens=(17, 0), S=3, I=2, bs=4, causal=True, shuffle=True):
+    return build("tiny", list(lens), R=R, H=H, num_shards=S, interleave=I, seed=seed,
+                 block_size=bs, causal=causal, shuffle=shuffle)
+
+
+def _run_oracle(w, S=None, I=None, causal=None):
+    return oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens,
+                                    w.num_shards if S is None else S,
+                                    w.interleave if I is None else I, w.scale,
+                                    w.causal if causal is None else causal)
+
+
+# ---------------------------------------------------------------- brute force
+
+BRUTE_CASES = [
+    # seed, B, R, H, lens, S, I, bs, causal
+    (11, 2, 3, 2, (17, 0), 3, 2, 4, True),
+    (12, 1, 4, 2, (40,), 5, 3, 8, True),
+    (13, 2, 1, 1, (9, 4), 2, 1, 4, False),
+    (14, 2, 4, 1, (3, 2), 4, 1, 4, True),    # rows with n = 0 at the short end
+    (15, 1, 2, 2, (33,), 1, 1, 8, False),
+    (16, 2, 2, 2, (25, 7), 5, 2, 4, True),   # several empty shards
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_oracle_matches_brute_force(case):
+    seed, B, R, H, lens, S, I, bs, causal = case
+    w = _tiny(seed, B=B, R=R, H=H, lens=lens, S=S, I=I, bs=bs, causal=causal)
+    got = _run_oracle(w)
+    out, lse, lse_sh, out_sh = _brute.brute_decode(
+        w.q_bits.tolist(), w.kv_bits.tolist(), w.block_table.tolist(), w.seq_lens.tolist(),
+        S, I, w.scale, causal)
+    np.testing.assert_allclose(got["out"], np.array(out), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["lse_final"], np.array(lse), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["lse_shard"], np.array(lse_sh), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["out_shard"], np.array(out_sh), rtol=0, atol=1e-12)
+    # the -inf pattern is exact
+    assert np.array_equal(np.isneginf(got["lse_shard"]), np.isneginf(np.array(lse_sh)))
+
+
+# ------------------------------------------------------------ library pin
+
+def _sdpa_reference(w, causal):
+    """torch float64 SDPA with an explicit boolean mask; V = K[..., :512]."""
+    B, R, H = w.B, w.R, w.H
+    out = np.zeros((B, R, H, 512))
+    lse = np.zeros((B, R, H))
+    for b in range(B):
+        L = int(w.seq_lens[b])
+        t = np.arange(L)
+        phys = w.block_table[b][t // w.block_size]
+        K = torch.from_numpy(oracle.bf16_bits_to_f64(w.kv_bits[phys, t % w.block_size]))
+        q = torch.from_numpy(oracle.bf16_bits_to_f64(w.q_bits[b]))  # [R, H, 576]
+        q = q.permute(1, 0, 2).contiguous()  # [H, R, 576]
+        r = torch.arange(R)[:, None]
+        allowed = torch.arange(L)[None, :] < (L - (R - 1 - r) if causal else torch.full_like(r, L))
+        if L == 0:
+            out[b] = 0.0
+            lse[b] = -np.inf
+            continue
+        Kh = K[None].expand(H, L, 576).contiguous()
+        Vh = K[None, :, :512].expand(H, L, 512).contiguous()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q, Kh, Vh, attn_mask=allowed[None].expand(H, R, L), scale=w.scale)
+        scores = w.scale * (q @ Kh.transpose(1, 2))
+        scores = scores.masked_fill(~allowed[None], float("-inf"))
+        l = torch.logsumexp(scores, dim=-1)
+        dead = ~allowed.any(dim=-1)  # rows with n = 0
+        o = o.permute(1, 0, 2).numpy().copy()
+        l = l.permute(1, 0).numpy().copy()
+        o[dead.numpy()] = 0.0
+        out[b] = o
+        lse[b] = l
+    return out, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_oracle_matches_torch_sdpa(causal):
+    w = build("pin", [300, 1, 77], R=4, H=3, num_shards=4, interleave=3, seed=21,
+              block_size=16, causal=causal)
+    got = _run_oracle(w)
+    ref_out, ref_lse = _sdpa_reference(w, causal)
+    np.testing.assert_allclose(got["out"], ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["lse_final"], ref_lse, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- closed forms
+
+def _manual(q_rows, keys, bs=4, S=1, I=1, causal=False, R=None):
+    """One request whose q rows and logical keys (float lists) are given exactly."""
+    keys = np.asarray(keys, dtype=np.float32)
+    n = keys.shape[0]
+    nb = max(1, (n + bs - 1) // bs)
+    kv = np.zeros((nb + 1, bs, 576), dtype=np.uint16)
+    table = np.zeros((1, nb), dtype=np.int32)
+    for j in range(nb):
+        table[0, j] = j + 1
+    for t in range(n):
+        kv[1 + t // bs, t % bs] = bf16_rne_bits(keys[t])
+    q = bf16_rne_bits(np.asarray(q_rows, dtype=np.float32))[None, :, None, :]  # [1, R, 1, 576]
+    return oracle.mla_decode_oracle(q, kv, table, np.array([n], np.int32), S, I, SCALE, causal)
+
+
+def test_closed_form_single_token():
+    rng = np.random.default_rng(1)
+    k = rng.integers(-4, 5, size=576).astype(np.float32)
+    q = rng.integers(-3, 4, size=576).astype(np.float32)
+    got = _manual([q], [k])
+    assert np.array_equal(got["out"][0, 0, 0], k[:512].astype(np.float64))
+    assert got["lse_final"][0, 0, 0] == pytest.approx(SCALE * float(q @ k), abs=1e-12)
+
+
+def test_closed_form_equal_keys():
+    rng = np.random.default_rng(2)
+    k = rng.integers(-4, 5, size=576).astype(np.float32)
+    q = rng.integers(-3, 4, size=576).astype(np.float32)
+    n = 37
+    got = _manual([q], [k] * n)
+    np.testing.assert_allclose(got["out"][0, 0, 0], k[:512], rtol=0, atol=1e-12)
+    assert got["lse_final"][0, 0, 0] == pytest.approx(SCALE * float(q @ k) + math.log(n), abs=1e-12)
+
+
+@pytest.mark.parametrize("S,I", [(1, 1), (3, 1), (4, 2), (5, 3), (8, 16)])
+def test_closed_form_zero_query(S, I):
+    """q = 0: every weight is 1, so lse_s = ln |T_s| and out_s = mean of V over T_s."""
+    rng = np.random.default_rng(3)
+    n = 50
+    keys = rng.integers(-8, 9, size=(n, 576)).astype(np.float32)
+    got = _manual([np.zeros(576, np.float32)], keys, S=S, I=I)
+    assert got["lse_final"][0, 0, 0] == pytest.approx(math.log(n), abs=1e-12)
+    np.testing.assert_allclose(got["out"][0, 0, 0], keys[:, :512].mean(axis=0), atol=1e-12)
+    for s in range(S):
+        members = [t for t in range(n) if ((t // I) % S) == s]
+        if not members:
+            assert got["lse_shard"][s, 0, 0, 0] == -np.inf
+            continue
+        assert got["lse_shard"][s, 0, 0, 0] == pytest.approx(math.log(len(members)), abs=1e-12)
+        np.testing.assert_allclose(got["out_shard"][s, 0, 0, 0],
+                                   keys[members, :512].mean(axis=0), atol=1e-12)
+
+
+def test_closed_form_two_tokens():
+    k0 = np.zeros(576, np.float32)
+    k1 = np.zeros(576, np.float32)
+    k0[0], k0[575] = 2.0, 1.0          # a rope column counts in the score
+    k1[0], k1[34] = -1.0, 3.0
+    q = np.zeros(576, np.float32)
+    q[0], q[575], q[34] = 1.5, 2.0, 0.5
+    got = _manual([q], [k0, k1])
+    a, b = SCALE * float(q @ k0), SCALE * float(q @ k1)
+    assert got["lse_final"][0, 0, 0] == pytest.approx(math.log(math.exp(a) + math.exp(b)), abs=1e-12)
+    wa = math.exp(a) / (math.exp(a) + math.exp(b))
+    np.testing.assert_allclose(got["out"][0, 0, 0], wa * k0[:512] + (1 - wa) * k1[:512], atol=1e-12)
+
+
+def test_empty_request_is_zero_and_neg_inf():
+    w = build("pad", [0, 5], R=2, H=2, num_shards=3, interleave=1, seed=4, block_size=4)
+    got = _run_oracle(w)
+    assert np.all(got["out"][0] == 0.0) and not np.signbit(got["out"][0]).any()
+    assert np.all(np.isneginf(got["lse_final"][0]))
+    assert np.all(np.isneginf(got["lse_shard"][:, 0]))
+
+
+# -------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("S", list(range(1, 10)))
+@pytest.mark.parametrize("I", [1, 2, 3, 16, 64])
+def test_split_then_merge_equals_unsplit(S, I):
+    w = build("inv", [130, 61], R=2, H=2, num_shards=S, interleave=I, seed=100 + S * 7 + I,
+              block_size=16)
+    got = _run_oracle(w)
+    out, lse = oracle.lse_combine_oracle(got["out_shard"], got["lse_shard"])
+    np.testing.assert_allclose(out, got["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, got["lse_final"], rtol=0, atol=1e-12)
+
+
+def test_single_shard_partial_is_whole():
+    w = build("one", [90], R=1, H=3, num_shards=1, interleave=5, seed=7, block_size=8)
+    got = _run_oracle(w)
+    np.testing.assert_array_equal(got["out_shard"][0], got["out"])
+    np.testing.assert_array_equal(got["lse_shard"][0], got["lse_final"])
+
+
+def test_empty_shards_change_nothing():
+    """S * I > n leaves shards empty; their -inf sources (NaN payload) drop out of the merge."""
+    w = build("emp", [5], R=1, H=2, num_shards=8, interleave=1, seed=8, block_size=4)
+    got = _run_oracle(w)
+    assert np.all(np.isneginf(got["lse_shard"][5:]))
+    poisoned = got["out_shard"].copy()
+    poisoned[5:] = np.nan
+    out, lse = oracle.lse_combine_oracle(poisoned, got["lse_shard"])
+    np.testing.assert_allclose(out, got["out"], atol=1e-12)
+    np.testing.assert_allclose(lse, got["lse_final"], atol=1e-12)
+    extra_o = np.concatenate([got["out_shard"], np.full((3,) + got["out_shard"].shape[1:], np.nan)])
+    extra_l = np.concatenate([got["lse_shard"], np.full((3,) + got["lse_shard"].shape[1:], -np.inf)])
+    out2, lse2 = oracle.lse_combine_oracle(extra_o, extra_l)
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(lse2, lse)
+
+
+def test_two_source_merge_closed_form():
+    a, b = 0.75, -2.5
+    oa, ob = np.full(512, 3.0), np.full(512, -1.0)
+    out, lse = oracle.lse_combine_oracle(np.stack([oa, ob])[:, None], np.array([[a], [b]]))
+    assert lse[0] == pytest.approx(math.log(math.exp(a) + math.exp(b)), abs=1e-14)
+    wa = math.exp(a) / (math.exp(a) + math.exp(b))
+    np.testing.assert_allclose(out[0], wa * oa + (1 - wa) * ob, atol=1e-14)
+
+
+def test_all_empty_merge():
+    out, lse = oracle.lse_combine_oracle(np.full((3, 2, 512), np.nan), np.full((3, 2), -np.inf))
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_block_layout_independence():
+    """Moving the physical blocks (and the table with them) changes no result bit."""
+    w = build("lay", [45, 64, 3], R=2, H=2, num_shards=3, interleave=2, seed=9, block_size=8)
+    rng = np.random.default_rng(10)
+    p = np.concatenate([[0], rng.permutation(w.num_blocks - 1) + 1])  # keep block 0 in place
+    kv2 = np.empty_like(w.kv_bits)
+    kv2[p] = w.kv_bits
+    table2 = p[w.block_table].astype(np.int32)
+    ga = _run_oracle(w)
+    gb = oracle.mla_decode_oracle(w.q_bits, kv2, table2, w.seq_lens, 3, 2, w.scale, True)
+    for key in ("out", "lse_final", "lse_shard", "out_shard"):
+        np.testing.assert_array_equal(ga[key], gb[key])
+
+
+# ------------------------------------------------------------- shard map
+
+def _local_length(n, S, I, s):
+    """Closed form of |{t < n : (t // I) mod S == s}|."""
+    full = n // (S * I)
+    rem = n % (S * I)
+    return full * I + min(I, max(0, rem - s * I))
+
+
+def test_shard_map_against_dealing():
+    for S in range(1, 17):
+        for I in (1, 2, 3, 5, 16, 64):
+            for n in list(range(0, 200)) + [511, 1000, 4095]:
+                owner = _brute.deal_tokens(n, S, I)
+                sets = oracle.shard_token_sets(n, S, I)
+                for s in range(S):
+                    members = [t for t in range(n) if owner[t] == s]
+                    assert sets[s].tolist() == members
+                    assert _local_length(n, S, I, s) == len(members)
+                    # local index j of shard s maps back to global token t
+                    for j, t in enumerate(members[:5]):
+                        assert (j // I) * S * I + s * I + (j % I) == t
+
+
+def test_padding_row_mask_semantics():
+    # requests: lengths 3, 0, 5, 0; query rows 1, 2, 1, 2
+    mask = oracle.padding_row_mask([3, 0, 5, 0], [0, 1, 3, 4, 6])
+    assert mask.tolist() == [False, True, True, False, True, True]
+
+
+# --------------------------------------------------------- planted mistakes
+
+def _drop_rope(q, K, scale):
+    q = np.asarray(q, dtype=np.float64)
+    K = K.copy()
+    K[:, 512:] = 0.0
+    return _orig_attention(q, K, scale)
+
+
+_orig_attention = mla_oracle.attention_row
+
+
+def _log2_lse(q, K, scale):
+    o, l = _orig_attention(q, K, scale)
+    return o, l / math.log(2.0)
+
+
+def _shard_ignores_interleave(n, S, I):
+    t = np.arange(n, dtype=np.int64)
+    return [t[(t % S) == s] for s in range(S)]
+
+
+def _off_by_one_rows(seq_len, R, r, causal):
+    n = int(seq_len) - (R - r) if causal else int(seq_len)
+    return max(n, 0)
+
+
+@pytest.mark.parametrize("mutation", ["drop_rope", "log2_lse", "shard_map", "causal_rows"])
+def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
+    """Each plausible oracle bug, planted on the CPU, makes a pin above fail."""
+    if mutation == "drop_rope":
+        monkeypatch.setattr(mla_oracle, "attention_row", _drop_rope)
+    elif mutation == "log2_lse":
+        monkeypatch.setattr(mla_oracle, "attention_row", _log2_lse)
+    elif mutation == "shard_map":
+        monkeypatch.setattr(mla_oracle, "shard_token_sets", _shard_ignores_interleave)
+    else:
+        monkeypatch.setattr(mla_oracle, "row_length", _off_by_one_rows)
+    caught = False
+    for case in BRUTE_CASES:
+        try:
+            test_oracle_matches_brute_force(case)
+        except AssertionError:
+            caught = True
+            break
+    if not caught:
+        try:
+            test_oracle_matches_torch_sdpa(True)
+        except AssertionError:
+            caught = True
+    assert caught, mutation

@@ -1,0 +1,13 @@
+"""Seeded synthetic workloads shared by the tests, the oracle checks and bench.py."""
+
+from .gen import (  # noqa: F401
+    Workload,
+    bf16_rne_bits,
+    build,
+    tiny,
+    batch_decode,
+    long_context,
+    verify,
+    padded,
+    STANDARD,
+)
