@@ -1,0 +1,190 @@
+"""Throughput of split-KV MLA decode + LSE combine on one MI355X.
+
+One step = one mla_split_decode call (partial-attention kernel + combine
+kernel) over one batch of synthetic inputs resident in HBM.  Default workload:
+the 120k-token long-context request (B=1, R=1, H=128, S=8 virtual shards,
+interleave 1, bf16 N(0,1), 64-token blocks).
+
+Timing: W warm-up steps, then exactly K steps captured in one HIP graph and
+replayed between two device synchronisations; ms_per_step is that wall time
+divided by K.  The K steps cycle through several copies of the KV cache whose
+total exceeds the 256 MB Infinity Cache, so KV bytes come from HBM.  The
+partial kernel's own duration is measured live with HIP events recorded by the
+library on its stream (eager steps), and gives the roofline fraction.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV tokens/s + HBM GB/s (% of peak) for split-KV MLA decode + LSE combine"
+HBM_PEAK_GBPS = 8000.0
+ROW_BYTES = 576 * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long",
+                    choices=["long", "long_b2", "batch", "verify", "padded", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--event-steps", type=int, default=20)
+    ap.add_argument("--min-kv-set-mb", type=float, default=640.0,
+                    help="cycle KV copies until the cycled set exceeds this many MB")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Unique KV rows + q + out + per-shard lse + lse_final, per step."""
+    rows = w.B * w.R * w.H
+    return (w.unique_kv_tokens * ROW_BYTES + rows * ROW_BYTES + rows * 512 * 2
+            + w.num_shards * rows * 4 + rows * 4)
+
+
+def kernel_bytes(w):
+    """What the partial kernel must read: unique KV rows and q."""
+    return w.unique_kv_tokens * ROW_BYTES + w.B * w.R * w.H * ROW_BYTES
+
+
+def cpu_baseline(w, budget_s):
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                 w.interleave, w.scale, w.causal)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (reps + 1) / reps > 3 * budget_s:
+            break
+    tokens = reps * int(w.seq_lens.astype(np.int64).sum())
+    return {"value": tokens / el, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full run(s) of the float64 oracle (unsplit + per-shard attention) "
+                      f"on this workload, {el:.1f} s, numpy BLAS threads = {threads}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the shards are virtual, on one device)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import split_kv_mla_amd as mla
+    import workloads
+
+    mla.load_library()
+    w = workloads.STANDARD[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    kv_host = torch.from_numpy(w.kv_bits.view(np.int16)).view(torch.bfloat16)
+    kv_mb = kv_host.numel() * 2 / 1e6
+    copies = max(1, math.ceil(args.min_kv_set_mb / kv_mb))
+    kvs = [kv_host.to(dev) for _ in range(copies)]
+    S, I = w.num_shards, w.interleave
+    a = mla.decode_args(q, kvs[0], bt, sl, S, I, w.scale, w.causal)
+    ws = mla.new_workspace(a, dev)
+    out = torch.empty((w.B, w.R, w.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((S, w.B, w.R, w.H), dtype=torch.float32, device=dev)
+    lf = torch.empty((w.B, w.R, w.H), dtype=torch.float32, device=dev)
+
+    def step(i, events=None):
+        mla.mla_split_decode(q, kvs[i % copies], bt, sl, S, I, w.scale, w.causal, out=out, lse=lse,
+                             lse_final=lf, workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-kernel durations from events the library records on its stream
+    part_ms, comb_ms = [], []
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.event_steps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        step(i, events=e)
+    torch.cuda.synchronize()
+    for e in evs:
+        part_ms.append(e[0].elapsed_time(e[1]))
+        comb_ms.append(e[1].elapsed_time(e[2]))
+
+    # K steps in one graph, replayed between synchronisations
+    K = args.steps
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()  # first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    tokens = int(w.seq_lens.astype(np.int64).sum())
+    value = tokens / (ms_per_step / 1e3)
+    alg = algorithmic_bytes(w)
+    part_avg = statistics.mean(part_ms)
+    kb = kernel_bytes(w)
+    achieved = kb / (part_avg / 1e3) / 1e9
+    step_gbps = alg / (ms_per_step / 1e3) / 1e9
+    flops = 2176.0 * w.B * w.R * w.H * (w.seq_lens.astype(np.int64).sum() / w.B)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, **{k: v for k, v in w.describe().items() if k != "workload"},
+                   "parallelism": "S virtual KV shards on one GPU"},
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "partial_kernel_ms": part_avg,
+        "combine_kernel_ms": statistics.mean(comb_ms),
+        "mfma_tflops_partial": flops / (part_avg / 1e3) / 1e12,
+        "kv_copies_cycled": copies,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "mla::partial_kernel", "bytes_per_launch": kb},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

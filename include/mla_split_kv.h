@@ -1,0 +1,140 @@
+/*
+ * mla_split_kv.h -- C ABI of the split-KV MLA decode library for MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Absorbed-latent MLA decode attention under decode context parallelism with
+ * virtual KV shards on one GPU.  Each query row attends over the paged latent
+ * KV cache of its request; a cache row is 576 bf16 values (512 latent + 64
+ * rope) and the attention value is the first 512 of them (the "MQA form" of
+ * the Kimi-K3 fused MLA layer: the prhub.com.cn summary of vLLM PR 50484,
+ * section "key source excerpts", the mla.py decode excerpt, where
+ * forward_mqa returns latent_out and lse).
+ *
+ * The request's tokens are dealt to S shards round-robin in units of the
+ * interleave size I: global token t belongs to shard (t / I) % S (the
+ * dcp_size * interleave alignment unit of the same summary, section
+ * "implementation breakdown" step 3).  Every shard yields a partial output
+ * and a log-sum-exp; the partials are merged with exp2 LSE weights, and an
+ * empty shard carries LSE = -inf and zero weight, its payload never read
+ * (vLLM PR 50484 page, "Summary"; the prhub summary, "implementation
+ * breakdown" step 4 and "risks" item 4).  Requests with seq_len 0 (graph
+ * padding) are masked the same way (PR 50484 page, "CUDA-graph padding
+ * follow-up").  R > 1 query rows per request are speculative verification
+ * rows that share the request's KV ("perf(mla): fuse K3 DCP verification
+ * queries", local-inference-lab/vllm PR 565 page, "Summary").
+ *
+ * Conventions
+ * -----------
+ * - LSE is the natural-log log-sum-exp, float32.
+ * - seq_lens[b] is the request's global length including its R new tokens.
+ *   With causal != 0, query row r (0 <= r < R) sees the first
+ *   seq_lens[b] - (R - 1 - r) tokens; otherwise every row sees seq_lens[b].
+ * - A row that sees no token yields out = +0.0 and LSE = -inf; a shard with
+ *   no token for a row yields that row's shard LSE = -inf exactly.
+ * - Every device buffer is caller-owned, contiguous, row-major, and stays
+ *   valid until the enqueued work completes.  Calls only enqueue work on
+ *   `stream` (a hipStream_t; NULL = the default stream) and return; they
+ *   never allocate and never synchronise.  Launch geometry depends only on
+ *   the scalar arguments, never on device data, so a call can be captured
+ *   in a HIP graph and replayed with changed seq_lens / block_table.
+ * - A negative return value means nothing was enqueued.
+ * - Device-detected input faults (a block id outside [0, num_blocks) in a
+ *   referenced table entry, seq_lens[b] outside [0, max_blocks_per_seq *
+ *   block_size]) produce NaN in every output of the affected request rather
+ *   than reading out of bounds.
+ */
+#ifndef MLA_SPLIT_KV_H
+#define MLA_SPLIT_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,         /* a null pointer, a bad size, or inconsistent sizes */
+  MLA_ERR_UNSUPPORTED = -2,         /* a shape outside what the kernels implement */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < mla_workspace_bytes(args) */
+  MLA_ERR_HIP = -4                  /* a HIP launch error */
+};
+
+enum { MLA_HEAD_DIM = 576, MLA_V_DIM = 512 };
+
+typedef struct mla_decode_args {
+  const void* q;              /* device bf16 [B, R, H, 576]                              */
+  const void* kv_cache;       /* device bf16 [num_blocks, block_size, 576]               */
+  const int32_t* block_table; /* device int32 [B, max_blocks_per_seq]: physical block ids */
+  const int32_t* seq_lens;    /* device int32 [B]; 0 marks a graph-padding request       */
+  int32_t batch;              /* B >= 0; B == 0 enqueues nothing and returns MLA_OK      */
+  int32_t rows;               /* R, query rows per request, 1..8                         */
+  int32_t heads;              /* H >= 1, R * H <= 1024                                   */
+  int32_t num_blocks;         /* physical blocks in kv_cache, >= 1                       */
+  int32_t block_size;         /* tokens per block: a power of two, 1..1024               */
+  int32_t max_blocks_per_seq; /* width of block_table, >= 1                              */
+  int32_t num_shards;         /* S >= 1                                                  */
+  int32_t interleave;         /* I >= 1: token t -> shard (t / I) % S                    */
+  float softmax_scale;        /* multiplies q.k before the softmax, e.g. 1/sqrt(192)     */
+  int32_t causal;             /* nonzero: verification rows see a causal tail            */
+} mla_decode_args;
+
+/* Bytes of device workspace the two decode entry points need for `a`
+ * (chunk partials of the split).  0 when the arguments are invalid. */
+size_t mla_workspace_bytes(const mla_decode_args* a);
+
+/* Partial attention of shards [shard_begin, shard_begin + shard_count): what
+ * one DCP rank computes for its own shard(s).  Writes
+ *   out_partial  float32 [shard_count, B, R, H, 512]: softmax over the shard's
+ *                tokens; left undefined where the shard is empty for a row;
+ *   lse          float32 [shard_count, B, R, H]: the shard's natural-log LSE,
+ *                exactly -inf where the shard is empty for a row.
+ * workspace: device memory of at least mla_workspace_bytes(a) bytes; its
+ * contents on entry do not matter. */
+int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count,
+                             float* out_partial, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* LSE-weighted merge of S partial states (the DCP combine):
+ *   out_partial  float32 [S, B, R, H, 512], lse float32 [S, B, R, H] (inputs);
+ *   out          bf16 [B, R, H, 512]: sum_s w_s * out_partial[s] / sum_s w_s
+ *                with w_s = exp2((lse_s - max_s lse_s) * log2(e)); sources
+ *                with lse = -inf are skipped and their out_partial never read;
+ *                +0.0 where every source is empty;
+ *   lse_final    float32 [B, R, H] or NULL: the merged natural-log LSE
+ *                (-inf where every source is empty).
+ * out may not alias out_partial. */
+int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
+                    int32_t rows, int32_t heads, void* out, float* lse_final, void* stream);
+
+/* The whole path: partial attention of every shard, then the LSE combine.
+ *   out        bf16 [B, R, H, 512]: attention over each row's whole KV;
+ *   lse        float32 [S, B, R, H]: per-shard LSE, exactly -inf where empty;
+ *   lse_final  float32 [B, R, H] or NULL: LSE over all shards.
+ * workspace as for mla_shard_decode_partial. */
+int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse_final,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_split_decode with measurement hooks: ev_begin, ev_mid and ev_end are
+ * hipEvent_t handles (each may be NULL) recorded on `stream` before the
+ * partial-attention kernel, between it and the combine kernel, and after the
+ * combine.  Same arguments, results and errors as mla_split_decode. */
+int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final,
+                           void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
+                           void* ev_mid, void* ev_end);
+
+/* A static string naming a status code. */
+const char* mla_status_string(int status);
+
+/* Number of chunk partials ("work items") per row group the decode entry
+ * points split the work into for `a`, and the row-group count: exposed for
+ * tests and measurement; -1 on invalid arguments. */
+int32_t mla_plan_capacity(const mla_decode_args* a, int32_t shard_count, int32_t* row_groups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_SPLIT_KV_H */

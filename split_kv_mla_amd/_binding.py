@@ -1,0 +1,235 @@
+"""ctypes binding of the C ABI in include/mla_split_kv.h.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity) and their data pointers handed to the HIP library together with
+the current HIP stream.  Every step of the computation runs in the library's
+kernels; there is no other code path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_split_kv.so")
+
+MLA_OK = 0
+HEAD_DIM = 576
+V_DIM = 512
+
+
+class MlaDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_shards", ctypes.c_int32),
+        ("interleave", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+    ]
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MlaError(f"{path} is missing: build it with `python split_kv_mla_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.mla_workspace_bytes.argtypes = [P(MlaDecodeArgs)]
+    lib.mla_workspace_bytes.restype = ctypes.c_size_t
+    lib.mla_plan_capacity.argtypes = [P(MlaDecodeArgs), ctypes.c_int32, P(ctypes.c_int32)]
+    lib.mla_plan_capacity.restype = ctypes.c_int32
+    lib.mla_shard_decode_partial.argtypes = [P(MlaDecodeArgs), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_shard_decode_partial.restype = ctypes.c_int
+    lib.mla_lse_combine.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.mla_lse_combine.restype = ctypes.c_int
+    lib.mla_split_decode.argtypes = [P(MlaDecodeArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_split_decode.restype = ctypes.c_int
+    lib.mla_split_decode_timed.argtypes = lib.mla_split_decode.argtypes + [ctypes.c_void_p] * 3
+    lib.mla_split_decode_timed.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        msg = load_library().mla_status_string(status).decode()
+        raise MlaError(f"split-KV MLA call failed: {msg} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _stream(device):
+    if device.type != "cuda":
+        raise ValueError("the split-KV MLA library runs on a GPU device")
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal=True):
+    """Validate the decode inputs and build the C argument struct."""
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError("q must be [B, R, H, 576]")
+    B, R, H, _ = q.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    if kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM:
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
+    _need(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    _need(block_table, "block_table", torch.int32, device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    a = MlaDecodeArgs()
+    a.q, a.kv_cache = q.data_ptr(), kv_cache.data_ptr()
+    a.block_table, a.seq_lens = block_table.data_ptr(), seq_lens.data_ptr()
+    a.batch, a.rows, a.heads = B, R, H
+    a.num_blocks, a.block_size = kv_cache.shape[0], kv_cache.shape[1]
+    a.max_blocks_per_seq = block_table.shape[1]
+    a.num_shards, a.interleave = int(num_shards), int(interleave)
+    a.softmax_scale = float(softmax_scale)
+    a.causal = 1 if causal else 0
+    return a
+
+
+def mla_workspace_bytes(args: MlaDecodeArgs) -> int:
+    return int(load_library().mla_workspace_bytes(ctypes.byref(args)))
+
+
+def mla_plan_capacity(args: MlaDecodeArgs, shard_count=None):
+    rg = ctypes.c_int32(0)
+    sc = args.num_shards if shard_count is None else shard_count
+    n = load_library().mla_plan_capacity(ctypes.byref(args), sc, ctypes.byref(rg))
+    return int(n), int(rg.value)
+
+
+def new_workspace(args: MlaDecodeArgs, device):
+    return torch.empty(max(1, mla_workspace_bytes(args)), dtype=torch.uint8, device=device)
+
+
+def mla_split_decode(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
+                     causal=True, out=None, lse=None, lse_final=None, workspace=None,
+                     want_lse_final=True, events=None):
+    """Split-KV decode of every shard plus the LSE combine.
+
+    ``events``: optional (begin, mid, end) torch.cuda.Event objects, already
+    recorded once, that the library records around its partial and combine
+    kernels (calls mla_split_decode_timed).
+    Returns (out bf16 [B,R,H,512], lse fp32 [S,B,R,H], lse_final fp32 [B,R,H] or None).
+    """
+    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal)
+    B, R, H, _ = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((num_shards, B, R, H), dtype=torch.float32, device=dev)
+    if lse_final is None and want_lse_final:
+        lse_final = torch.empty((B, R, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, (B, R, H, V_DIM), dev)
+    _need(lse, "lse", torch.float32, (num_shards, B, R, H), dev)
+    if lse_final is not None:
+        _need(lse_final, "lse_final", torch.float32, (B, R, H), dev)
+    if workspace is None:
+        workspace = new_workspace(a, dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    lib = load_library()
+    if events is None:
+        _check(lib.mla_split_decode(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(lse_final),
+                                    _ptr(workspace), workspace.numel(), _stream(dev)))
+    else:
+        handles = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
+        _check(lib.mla_split_decode_timed(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(lse_final),
+                                          _ptr(workspace), workspace.numel(), _stream(dev), *handles))
+    return out, lse, lse_final
+
+
+def mla_shard_decode_partial(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
+                             causal=True, shard_begin=0, shard_count=None, out_partial=None, lse=None,
+                             workspace=None):
+    """Partial attention of shards [shard_begin, shard_begin + shard_count).
+
+    Returns (out_partial fp32 [shard_count,B,R,H,512], lse fp32 [shard_count,B,R,H]).
+    """
+    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal)
+    B, R, H, _ = q.shape
+    dev = q.device
+    sc = num_shards - shard_begin if shard_count is None else shard_count
+    if out_partial is None:
+        out_partial = torch.empty((sc, B, R, H, V_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((sc, B, R, H), dtype=torch.float32, device=dev)
+    _need(out_partial, "out_partial", torch.float32, (sc, B, R, H, V_DIM), dev)
+    _need(lse, "lse", torch.float32, (sc, B, R, H), dev)
+    if workspace is None:
+        workspace = new_workspace(a, dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    _check(load_library().mla_shard_decode_partial(ctypes.byref(a), shard_begin, sc, _ptr(out_partial),
+                                                   _ptr(lse), _ptr(workspace), workspace.numel(),
+                                                   _stream(dev)))
+    return out_partial, lse
+
+
+def mla_lse_combine(out_partial, lse, out=None, lse_final=None, want_lse_final=True):
+    """LSE-weighted merge of S partials: out_partial fp32 [S,B,R,H,512], lse fp32 [S,B,R,H].
+
+    Returns (out bf16 [B,R,H,512], lse_final fp32 [B,R,H] or None).
+    """
+    if out_partial.dim() != 5 or out_partial.shape[-1] != V_DIM:
+        raise ValueError("out_partial must be [S, B, R, H, 512]")
+    S, B, R, H, _ = out_partial.shape
+    dev = out_partial.device
+    _need(out_partial, "out_partial", torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, (S, B, R, H), dev)
+    if out is None:
+        out = torch.empty((B, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse_final is None and want_lse_final:
+        lse_final = torch.empty((B, R, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, (B, R, H, V_DIM), dev)
+    if lse_final is not None:
+        _need(lse_final, "lse_final", torch.float32, (B, R, H), dev)
+    _check(load_library().mla_lse_combine(_ptr(out_partial), _ptr(lse), S, B, R, H, _ptr(out),
+                                          _ptr(lse_final), _stream(dev)))
+    return out, lse_final

@@ -1,0 +1,621 @@
+// mla_kernels.h -- HIP kernels for gfx950 (CDNA4): split-KV MLA decode partials
+// and the exp2 LSE-weighted combine.
+//
+// Partial kernel (one workgroup = 4 wavefronts = one work item x one group of
+// 128 query rows):
+//   * every workgroup derives the same work plan from seq_lens on the device:
+//     each (request, shard) pair's local tokens are cut into 32-token tiles and
+//     the tiles into items of equal length;
+//   * KV tiles (32 tokens x 576 bf16 = 36 KiB) stream HBM -> LDS with 16-byte
+//     direct-to-LDS loads through a 4-deep ring, so three tiles are in flight
+//     while one is consumed; the whole tile is shared by the four wavefronts;
+//   * S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 32x32x16 with fp32
+//     accumulation; P enters as a bf16 pair P_hi + P_lo (two MFMAs on the
+//     same V fragment) so the weights keep ~16 bits.  K rows come from LDS with ds_read_b128, V columns with the
+//     transposing ds_read_b64_tr_b16, Q lives in VGPRs, the 32x512 accumulator
+//     of a wavefront in (A)VGPRs.  V is the first 512 columns of the same
+//     tile: it is never loaded twice;
+//   * online softmax in fp32 on base-2 scores, with lazy rescaling (the
+//     running max moves only when a tile's max exceeds it by 2^8);
+//   * each item writes a normalised partial output and its natural-log LSE;
+//     an item that holds no token of a row writes LSE = -inf and no output.
+// Combine kernel: one workgroup per (request, row, 128-wide slice of the 512
+// output columns) merges the item partials with weights
+// exp2((lse_i - max lse) * log2 e), skipping -inf sources, and writes the
+// bf16 output, the per-shard LSEs and the merged LSE.
+//
+// The method: vLLM PR 50484 ("[Kimi-K3] DCP support") page, "Summary", and its
+// prhub.com.cn summary, "implementation breakdown" step 4 (partial output +
+// LSE per shard, source-side -inf mask, consumer-side zero-weight skip, exp2
+// LSE-weighted merge); the R verification rows of a request share every KV
+// tile load (local-inference-lab/vllm PR 565 page, "Summary").
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
+constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
+constexpr int kRowsPerGroup = 4 * kRowsPerWave;   // 128 query rows per workgroup
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct DecodeParams {
+  const uint16_t* q;         // bf16 [B, R, H, 576]
+  const uint16_t* kv;        // bf16 [num_blocks, block_size, 576]
+  const int32_t* table;      // [B, max_blocks]
+  const int32_t* seq_lens;   // [B]
+  void* part_o;              // [items_cap, rows_total, 512] fp32 or bf16
+  float* part_lse;           // [items_cap, rows_total]
+  int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, tiles per item
+  int32_t B, R, H, rows_total, row_groups;
+  int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
+  int32_t S, I, shard_begin, shard_count, pairs;
+  int32_t items_cap, tpi_min, tpi_max;
+  float c_log2;              // softmax_scale * log2(e)
+  int32_t causal;
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Exclusive prefix over the workgroup's 256 threads; `total` gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int incl = wave_incl_scan(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) scratch[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    const int x = scratch[i];
+    off += (i < w) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+// Request length with out-of-range values treated as empty (the combine
+// reports those requests as NaN).
+__device__ __forceinline__ int32_t checked_len(const int32_t* seq_lens, int b, int cap) {
+  const int32_t L = seq_lens[b];
+  return (L < 0 || L > cap) ? 0 : L;
+}
+
+// Tiles of (request, shard) pair `pr`: its longest row sees the whole request.
+__device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
+  const int b = pr / p.shard_count;
+  const int s = p.shard_begin + pr % p.shard_count;
+  const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
+  return ceil_div(local_len(L, p.S, p.I, s), kTile);
+}
+
+struct ItemInfo {
+  int pair;   // -1: no work for this item slot
+  int k;      // item index within its pair
+  int tpi;    // tiles per item
+};
+
+// Every workgroup computes the same plan; workgroup 0 also publishes it.
+__device__ ItemInfo locate_item(const DecodeParams& p, int item, int* scratch) {
+  int total = 0;
+  for (int base = 0; base < p.pairs; base += kThreads) {
+    const int pr = base + (int)threadIdx.x;
+    const int t = pr < p.pairs ? pair_tiles(p, pr) : 0;
+    int tot;
+    block_excl_scan(t, scratch, &tot);
+    total += tot;
+  }
+  const int tpi = tiles_per_item(total, p.items_cap, p.pairs, p.tpi_min, p.tpi_max);
+  if (threadIdx.x == 0) { scratch[8] = -1; scratch[9] = 0; }
+  int start = 0;
+  const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
+  for (int base = 0; base < p.pairs; base += kThreads) {
+    const int pr = base + (int)threadIdx.x;
+    const int t = pr < p.pairs ? pair_tiles(p, pr) : 0;
+    const int cnt = ceil_div(t, tpi);
+    int tot;
+    const int my0 = start + block_excl_scan(cnt, scratch, &tot);
+    if (pr < p.pairs) {
+      if (publish) p.plan_out[pr] = my0;
+      if (item >= my0 && item < my0 + cnt) { scratch[8] = pr; scratch[9] = item - my0; }
+    }
+    start += tot;
+  }
+  if (publish && threadIdx.x == 0) { p.plan_out[p.pairs] = start; p.plan_out[p.pairs + 1] = tpi; }
+  __syncthreads();
+  ItemInfo info;
+  info.pair = scratch[8];
+  info.k = scratch[9];
+  info.tpi = tpi;
+  return info;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// ------------------------------------------------------------ partial kernel
+
+template <bool kBf16Part>
+__global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
+  __shared__ int tbl[kTableCache];
+  __shared__ int scratch[16];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 5;      // which half of the wavefront
+  const int l32 = lane & 31;
+
+  // Item and row group.  With several row groups, the groups of one item get
+  // block ids congruent mod 8, i.e. the same XCD and its L2.
+  int item, rg;
+  if (p.row_groups == 1) {
+    item = blockIdx.x;
+    rg = 0;
+  } else {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    rg = k % p.row_groups;
+    item = (k / p.row_groups) * 8 + x;
+  }
+  if (item >= p.items_cap) return;
+
+  const ItemInfo info = locate_item(p, item, scratch);
+  if (info.pair < 0) return;
+  const int b = info.pair / p.shard_count;
+  const int s = p.shard_begin + info.pair % p.shard_count;
+  const int S = p.S, I = p.I;
+  const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
+  const int n_bs = local_len(L, S, I, s);
+  const int tile0 = info.k * info.tpi;
+  const int tile1 = min(tile0 + info.tpi, ceil_div(n_bs, kTile));
+  const int nt = tile1 - tile0;
+  const int bs_mask = (1 << p.bs_log2) - 1;
+
+  // Block-table window of this item (fits kTableCache by the choice of tpi_max).
+  const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
+  const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
+  const int span = blk_hi - blk_lo + 1;
+  bool bad = false;
+  for (int i = tid; i < span; i += kThreads) {
+    int v = p.table[(size_t)b * p.max_blocks + blk_lo + i];
+    if ((unsigned)v >= (unsigned)p.num_blocks) { v = 0; bad = true; }
+    tbl[i] = v;
+  }
+
+  // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
+  const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
+  const bool row_ok = row < p.rows_total;
+  const int r = row_ok ? row / p.H : 0;
+  const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
+  const int lim_min = wave_min(lim);
+
+  // Q^T operand: lane holds row l32, columns 16*db + 8*g .. +7 for db < 36.
+  bf16x8 qf[36];
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + (row_ok ? row : 0)) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int db = 0; db < 36; ++db) {
+      if (row_ok)
+        qf[db] = *reinterpret_cast<const bf16x8*>(qrow + 16 * db);
+      else
+        qf[db] = bf16x8{};
+    }
+  }
+  bad = __syncthreads_or(bad);
+  // Q must be resident before the LDS ring starts counting loads.
+#pragma unroll
+  for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
+  wait_vmcnt<0>();
+
+  // DMA role: lane loads token tau of each tile, 16-byte pieces (lane & 7) ^ swz
+  // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
+  //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ ((tau >> 1) & 7))
+  const int dma_tau = wave * 8 + (lane >> 3);
+  const int dma_swz = ((lane & 7) ^ ((dma_tau >> 1) & 7)) * 16;
+  auto issue_tile = [&](int kk, int stage) {
+    int j = kk * kTile + dma_tau;
+    j = j < n_bs ? j : n_bs - 1;  // rows past the end re-read the last valid row (masked later)
+    const int t = global_pos(j, S, I, s);
+    const int phys = tbl[(t >> p.bs_log2) - blk_lo];
+    const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
+    const char* src = reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
+    char* dst = ring + stage * kTileBytes + wave * 9 * 1024;
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      __builtin_amdgcn_global_load_lds(src + 128 * i, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  };
+
+  // K-read (A of S^T = K Q^T): lane reads token l32, piece 2*db + g.
+  const int kswz = (l32 >> 1) & 7;
+  const int kbase = (576 * (l32 >> 3) + 8 * (l32 & 7)) * 16;
+  int koff[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) koff[d] = kbase + (((2 * d + g) ^ kswz) * 16);
+  // V-read (A of O^T = V^T P^T) with the transposing read: 16-lane group
+  // (g, h) covers columns 32*db + 16*h .. +15 of tokens {4g+r} and {8+4g+r}.
+  const int h16 = (lane >> 4) & 1;
+  const int rr = (lane & 15) >> 2;
+  const int cc = lane & 3;
+  const int f1 = (2 * g + (rr >> 1)) & 7;
+  const int f2 = (4 + 2 * g + (rr >> 1)) & 7;
+  int voff1[2], voff2[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int pc = 4 * e + 2 * h16 + (cc >> 1);
+    voff1[e] = 128 * (4 * g + rr) + 16 * (pc ^ f1) + 8 * (cc & 1);
+    voff2[e] = 9216 + 128 * (4 * g + rr) + 16 * (pc ^ f2) + 8 * (cc & 1);
+  }
+
+  f32x16 acc[16];
+  float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
+  float l_run = 0.f;
+  const float c = p.c_log2;
+
+  // One pipelined walk over the item's tiles.  kMaxOnly: only the exact row
+  // maximum of the scores (written to m_ref).  Otherwise the softmax
+  // numerator and denominator against m_ref; m_ref is taken from the first
+  // tile that holds a token of the row, and a later tile whose maximum exceeds
+  // it by more than kSlack (a possible fp32 overflow of the sums) sets
+  // `overflow` instead of rescaling the accumulators.
+  constexpr float kSlack = 64.f;
+  auto walk = [&](auto max_only_tag, bool& overflow) {
+    constexpr bool kMaxOnly = decltype(max_only_tag)::value;
+    const int pre = min(nt, kStages - 1);
+    for (int k = 0; k < pre; ++k) issue_tile(tile0 + k, k);
+    float m_walk = -INFINITY;
+    for (int k = 0; k < nt; ++k) {
+      // tile k resident: at most min(nt-1-k, kStages-2) younger tiles in flight
+      const int younger = min(nt - 1 - k, kStages - 2);
+      if (younger >= 2) wait_vmcnt<18>();
+      else if (younger == 1) wait_vmcnt<9>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (k + kStages - 1 < nt) issue_tile(tile0 + k + kStages - 1, (k + kStages - 1) % kStages);
+      const char* buf = ring + (k % kStages) * kTileBytes;
+
+      // S^T[token][row] for 32 tokens x 32 rows.
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int db = 0; db < 36; ++db) {
+        if ((db & 3) == 0) asm volatile("" ::: "memory");  // bound how far LDS reads run ahead
+        const bf16x8 a = lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[db], sc, 0, 0, 0);
+      }
+      // lane holds row l32 and tokens 8*(i/4) + 4*g + (i%4)
+      const int jt = (tile0 + k) * kTile;
+      if (jt + kTile > lim_min) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = jt + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (j >= lim) sc[i] = -INFINITY;
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      if constexpr (kMaxOnly) {
+        m_walk = fmaxf(m_walk, mx);
+        continue;
+      } else {
+        if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet: no rescale needed
+        overflow |= mx > m_ref + kSlack;
+        const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
+        float pv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -msafe));
+          l_run += pv[i];
+        }
+        // P = P_hi + P_lo, both bf16: a single bf16 P would cost up to 2^-8 of
+        // relative weight per token, too much for rows of a few tokens or with
+        // outlier values; the pair leaves a residual of at most 2^-16 p.
+        bf16x8 pb[2], pl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = pv[8 * kb + j];
+            const __bf16 hi = (__bf16)x;
+            pb[kb][j] = hi;
+            pl[kb][j] = (__bf16)(x - (float)hi);
+          }
+
+        // O^T[dim][row] += V^T[dim][token] P^T[token][row]
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int db = 0; db < 16; ++db) {
+            if ((db & 3) == 0) asm volatile("" ::: "memory");
+            const int off = 18432 * kb + 1024 * (db >> 1);
+            const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
+            const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl[kb], acc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if constexpr (kMaxOnly) m_ref = m_walk;
+  };
+
+  using MaxOnly = std::integral_constant<bool, true>;
+  using Full = std::integral_constant<bool, false>;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
+  bool overflow = false;
+  walk(Full{}, overflow);
+  if (__syncthreads_or(overflow)) {
+    // Rare slow path: scores grew by more than 2^64 after the reference was
+    // fixed.  Find each row's exact maximum, then redo the walk against it.
+    bool unused = false;
+    walk(MaxOnly{}, unused);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
+    l_run = 0.f;
+    const float m_exact = m_ref;
+    walk(Full{}, unused);
+    m_ref = m_exact;
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const size_t prow = (size_t)item * p.rows_total + row;
+  float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  if (bad) lse = __builtin_nanf("");
+  if (g == 0) p.part_lse[prow] = lse;
+  if (!(l_tot > 0.f)) return;
+  const float inv = 1.f / l_tot;
+  // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3]
+  if constexpr (kBf16Part) {
+    __bf16* po = reinterpret_cast<__bf16*>(p.part_o) + prow * kVDim + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * q + e] * inv);
+        *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * q) = v;
+      }
+  } else {
+    float* po = reinterpret_cast<float*>(p.part_o) + prow * kVDim + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q) = v;
+      }
+  }
+}
+
+// ------------------------------------------------------------ combine kernel
+
+enum CombineMode : int32_t {
+  kCombineItems = 0,   // merge all items of a request: bf16 out, per-shard lse, lse_final
+  kMergeShard = 1,     // merge the items of one (request, shard): fp32 out_partial, shard lse
+  kCombineShards = 2,  // merge caller-provided shard partials: bf16 out, lse_final
+};
+
+struct CombineParams {
+  const void* src_o;        // items: [items_cap, rows, 512]; shards: [S, B, rows, 512] fp32
+  const float* src_lse;     // items: [items_cap, rows]; shards: [S, B, rows]
+  const int32_t* plan;      // [pairs + 2] from the partial kernel (item modes)
+  const int32_t* seq_lens;  // [B] (item modes; NULL in kCombineShards)
+  int32_t cap_tokens;
+  int32_t items_cap;        // item slots in src_o / src_lse (item modes)
+  void* out;                // bf16 [B, rows, 512] or fp32 [shard_count, B, rows, 512]
+  float* lse_shard;         // [shard_count, B, rows]
+  float* lse_final;         // [B, rows] or NULL
+  int32_t B, rows, shard_count, mode;
+};
+
+__device__ __forceinline__ float nan_max(float a, float b) {
+  return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
+}
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+  // 256 threads -> one value, broadcast
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float u = __shfl_xor(v, d, 64);
+    v = is_max ? nan_max(v, u) : v + u;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = is_max ? nan_max(r, red[i]) : r + red[i];
+  return r;
+}
+
+template <bool kBf16Part>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
+  __shared__ f32x4 part[8][32];
+  __shared__ float red[8];
+
+  const int tid = threadIdx.x;
+  const int quarter = blockIdx.x & 3;
+  int unit = blockIdx.x >> 2;
+  const int row = unit % p.rows;
+  unit /= p.rows;
+  const int b = unit % p.B;
+  const int s_out = unit / p.B;  // kMergeShard: shard (relative); otherwise 0
+
+  // Sources [i0, i1) and how to address them.
+  int i0, i1;
+  size_t o_stride, l_stride, o_base, l_base;
+  bool bad = false;
+  if (p.mode == kCombineShards) {
+    i0 = 0;
+    i1 = p.shard_count;
+    l_stride = (size_t)p.B * p.rows;
+    l_base = (size_t)b * p.rows + row;
+    o_stride = l_stride * kVDim;
+    o_base = l_base * kVDim;
+  } else {
+    const int SC = p.shard_count;
+    const int pr0 = b * SC + (p.mode == kMergeShard ? s_out : 0);
+    const int pr1 = p.mode == kMergeShard ? pr0 + 1 : (b + 1) * SC;
+    i0 = p.plan[pr0];
+    i1 = p.plan[pr1];   // plan[pairs] is the total item count
+    if (i0 < 0 || i1 < i0 || i1 > p.items_cap) {  // a plan that does not fit its slots: report, never read
+      i0 = i1 = 0;
+      bad = true;
+    }
+    l_stride = (size_t)p.rows;
+    l_base = row;
+    o_stride = l_stride * kVDim;
+    o_base = (size_t)row * kVDim;
+    const int32_t L = p.seq_lens[b];
+    bad = bad || L < 0 || L > p.cap_tokens;
+  }
+
+  // pass 1: max and total weight
+  float m = -INFINITY;
+  for (int i = i0 + tid; i < i1; i += kThreads) m = nan_max(m, p.src_lse[l_base + (size_t)i * l_stride]);
+  m = block_reduce(m, true, red);
+  bad = bad || (m != m);
+  const bool empty = (m == -INFINITY);
+  float wsum = 0.f;
+  if (!bad && !empty)
+    for (int i = i0 + tid; i < i1; i += kThreads) {
+      const float x = p.src_lse[l_base + (size_t)i * l_stride];
+      if (x != -INFINITY) wsum += __builtin_amdgcn_exp2f((x - m) * kLog2e);
+    }
+  wsum = block_reduce(wsum, false, red);
+
+  // pass 2: weighted sum of this block's 128 columns
+  const int sg = tid >> 5;        // source group
+  const int col = quarter * 128 + 4 * (tid & 31);
+  f32x4 acc = f32x4{};
+  if (!bad && !empty) {
+    for (int i = i0 + sg; i < i1; i += 8) {
+      const float x = p.src_lse[l_base + (size_t)i * l_stride];
+      if (x == -INFINITY) continue;  // empty source: its payload is never read
+      const float w = __builtin_amdgcn_exp2f((x - m) * kLog2e);
+      const size_t off = o_base + (size_t)i * o_stride + col;
+      f32x4 v;
+      if (kBf16Part && p.mode != kCombineShards) {
+        const bf16x4 hv = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.src_o) + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)hv[e];
+      } else {
+        v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.src_o) + off);
+      }
+      acc += w * v;
+    }
+  }
+  part[sg][tid & 31] = acc;
+  __syncthreads();
+
+  if (tid < 32) {
+    f32x4 t = part[0][tid];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) t += part[j][tid];
+    const float inv = 1.f / wsum;
+    f32x4 o;
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = bad ? qnan : (empty ? 0.f : t[e] * inv);
+    const size_t orow = (size_t)b * p.rows + row;
+    if (p.mode == kMergeShard) {
+      float* out = reinterpret_cast<float*>(p.out) + ((size_t)s_out * p.B * p.rows + orow) * kVDim + col;
+      *reinterpret_cast<f32x4*>(out) = o;
+    } else {
+      __bf16* out = reinterpret_cast<__bf16*>(p.out) + orow * kVDim + col;
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
+      *reinterpret_cast<bf16x4*>(out) = ob;
+    }
+  }
+  if (quarter != 0) return;
+
+  const float qnan = __builtin_nanf("");
+  const float lse_all = bad ? qnan : (empty ? -INFINITY : m + __builtin_amdgcn_logf(wsum) * kLn2);
+  const size_t orow = (size_t)b * p.rows + row;
+  if (p.mode == kMergeShard) {
+    if (tid == 0) p.lse_shard[(size_t)s_out * p.B * p.rows + orow] = lse_all;
+    return;
+  }
+  if (tid == 0 && p.lse_final) p.lse_final[orow] = lse_all;
+  if (p.mode != kCombineItems) return;
+  // per-shard LSE over each shard's items: one wavefront per shard
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int s = wave; s < p.shard_count; s += kThreads / 64) {
+    const int a0 = p.plan[b * p.shard_count + s];
+    const int a1 = p.plan[b * p.shard_count + s + 1];
+    float ms = -INFINITY;
+    for (int i = a0 + lane; i < a1; i += 64) ms = nan_max(ms, p.src_lse[(size_t)i * p.rows + row]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ms = nan_max(ms, __shfl_xor(ms, d, 64));
+    float ws = 0.f;
+    if (ms == ms && ms != -INFINITY)
+      for (int i = a0 + lane; i < a1; i += 64) {
+        const float x = p.src_lse[(size_t)i * p.rows + row];
+        if (x != -INFINITY) ws += __builtin_amdgcn_exp2f((x - ms) * kLog2e);
+      }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ws += __shfl_xor(ws, d, 64);
+    if (lane == 0) {
+      float v = (ms != ms || bad) ? qnan : (ms == -INFINITY ? -INFINITY : ms + __builtin_amdgcn_logf(ws) * kLn2);
+      p.lse_shard[(size_t)s * p.B * p.rows + orow] = v;
+    }
+  }
+}
+
+}  // namespace mla

@@ -1,0 +1,80 @@
+// mla_plan.h -- shard geometry and the split of the KV walk into work items.
+//
+// Shared by the host entry points (sizing) and the kernels (each workgroup
+// derives the same plan from seq_lens on the device, so launch geometry never
+// depends on device data).
+//
+// Shard map: global token t of a request belongs to shard (t / I) % S, so KV
+// is dealt to shards round-robin in units of the interleave size I (the
+// dcp_size * interleave alignment unit of the prhub.com.cn summary of vLLM
+// PR 50484, "implementation breakdown" step 3).  Local index j of shard s is
+// global token (j / I) * S * I + s * I + j % I.
+#pragma once
+
+#include <stdint.h>
+
+#define MLA_HD __host__ __device__ __forceinline__
+
+namespace mla {
+
+constexpr int kHeadDim = 576;       // 512 latent + 64 rope
+constexpr int kVDim = 512;          // V is the first 512 columns of a cache row
+constexpr int kTile = 32;           // KV tokens per MFMA tile
+constexpr int kRowsPerWave = 32;    // query rows one wavefront owns
+constexpr int kTableCache = 2048;   // block-table entries one work item may span
+constexpr int kThreads = 256;       // threads per partial / combine workgroup
+
+// Tokens of a request of n tokens that land in shard s.
+MLA_HD int32_t local_len(int32_t n, int32_t S, int32_t I, int32_t s) {
+  const int64_t unit = (int64_t)S * I;
+  const int64_t full = n / unit;
+  int64_t extra = (int64_t)(n % unit) - (int64_t)s * I;
+  extra = extra < 0 ? 0 : (extra > I ? I : extra);
+  return (int32_t)(full * I + extra);
+}
+
+// Global position of local token j of shard s.
+MLA_HD int32_t global_pos(int32_t j, int32_t S, int32_t I, int32_t s) {
+  return (j / I) * S * I + s * I + j % I;
+}
+
+// Number of KV tokens query row r (of R) sees in a request of seq_len tokens.
+MLA_HD int32_t row_len(int32_t seq_len, int32_t R, int32_t r, int32_t causal) {
+  const int32_t n = causal ? seq_len - (R - 1 - r) : seq_len;
+  return n < 0 ? 0 : n;
+}
+
+MLA_HD int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Upper bound on the block-table entries spanned by `tiles` consecutive tiles
+// of one shard's local tokens.
+MLA_HD int64_t table_span(int64_t tiles, int32_t S, int32_t I, int32_t block_size) {
+  const int64_t units = (tiles * kTile + I - 1) / I + 1;  // interleave units touched
+  const int64_t tokens = units * S * I;                   // global positions they cover
+  return tokens / block_size + 2;
+}
+
+// Largest tiles-per-item whose table span fits kTableCache.
+inline int32_t max_tiles_per_item(int32_t S, int32_t I, int32_t block_size) {
+  int32_t lo = 1, hi = 1 << 20;
+  if (table_span(1, S, I, block_size) > kTableCache) return 0;
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo + 1) / 2;
+    if (table_span(mid, S, I, block_size) <= kTableCache) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Tiles per item for a launch: spread `total_tiles` over the item slots that
+// remain after every (request, shard) pair has had one slot for its rounding.
+MLA_HD int32_t tiles_per_item(int32_t total_tiles, int32_t items_cap, int32_t pairs,
+                              int32_t tpi_min, int32_t tpi_max) {
+  int32_t free_slots = items_cap - pairs;
+  if (free_slots < 1) free_slots = 1;
+  int32_t tpi = ceil_div(total_tiles > 0 ? total_tiles : 1, free_slots);
+  if (tpi < tpi_min) tpi = tpi_min;
+  if (tpi > tpi_max) tpi = tpi_max;
+  return tpi;
+}
+
+}  // namespace mla

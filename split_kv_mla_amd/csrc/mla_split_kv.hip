@@ -1,0 +1,269 @@
+// mla_split_kv.hip -- host side of the C ABI declared in include/mla_split_kv.h:
+// argument checks, workspace sizing, the item plan's capacity, and launches.
+// Every call only enqueues kernels on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstdlib>
+#include <algorithm>
+
+#include "mla_kernels.h"
+#include "mla_split_kv.h"
+
+namespace {
+
+using mla::ceil_div;
+
+// Workgroups the partial kernel aims to keep busy: one per compute unit of
+// an MI355X (256 CUs), each holding one 4-wave workgroup.
+int target_workgroups() {
+  static int cached = 0;
+  if (cached == 0) {
+    int v = 256;
+    if (const char* e = std::getenv("MLA_SPLIT_KV_TARGET_WGS")) {
+      const int x = std::atoi(e);
+      if (x > 0 && x <= (1 << 20)) v = x;
+    }
+    cached = v;
+  }
+  return cached;
+}
+
+bool partials_in_bf16() {
+  const char* e = std::getenv("MLA_SPLIT_KV_PARTIAL_BF16");
+  return e && e[0] == '1';
+}
+
+int ilog2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+int check_args(const mla_decode_args* a) {
+  if (!a) return MLA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->rows < 1 || a->heads < 1 || a->num_blocks < 1 || a->max_blocks_per_seq < 1 ||
+      a->num_shards < 1 || a->interleave < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!(a->softmax_scale > 0.f) || !std::isfinite(a->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (a->batch > 0 && (!a->q || !a->kv_cache || !a->block_table || !a->seq_lens)) return MLA_ERR_INVALID_ARG;
+  if (a->rows > 8 || (int64_t)a->rows * a->heads > 1024) return MLA_ERR_UNSUPPORTED;
+  const int lg = ilog2_exact(a->block_size);
+  if (lg < 0 || a->block_size > 1024) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->max_blocks_per_seq * a->block_size > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->num_shards * a->interleave > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->num_blocks * a->block_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->batch * a->num_shards > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  if (mla::max_tiles_per_item(a->num_shards, a->interleave, a->block_size) < 1) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+struct Plan {
+  int32_t pairs, row_groups, items_cap, tpi_min, tpi_max;
+  size_t plan_bytes, lse_bytes, o_bytes;
+  size_t total() const { return plan_bytes + lse_bytes + o_bytes; }
+};
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Capacity of the item plan: enough slots that the device-side split, whatever
+// the lengths, never produces more items than the grid has workgroups for.
+Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count) {
+  Plan p{};
+  const int32_t rows_total = a->rows * a->heads;
+  p.pairs = a->batch * shard_count;
+  p.row_groups = ceil_div(rows_total, mla::kRowsPerGroup);
+  p.tpi_max = mla::max_tiles_per_item(a->num_shards, a->interleave, a->block_size);
+  p.tpi_min = 1;
+  const int32_t cap_tokens = a->max_blocks_per_seq * a->block_size;
+  int64_t cap_tiles = 0;
+  for (int32_t s = shard_begin; s < shard_begin + shard_count; ++s)
+    cap_tiles += ceil_div(mla::local_len(cap_tokens, a->num_shards, a->interleave, s), mla::kTile);
+  cap_tiles *= a->batch;
+  const int64_t need = (cap_tiles + p.tpi_max - 1) / p.tpi_max + p.pairs;
+  const int64_t target = std::max<int64_t>(1, target_workgroups() / p.row_groups) + p.pairs;
+  p.items_cap = (int32_t)std::max<int64_t>(need, target);
+  const size_t part_elem = partials_in_bf16() ? 2 : 4;
+  p.plan_bytes = round_up(sizeof(int32_t) * (size_t)(p.pairs + 2), 256);
+  p.lse_bytes = round_up(sizeof(float) * (size_t)p.items_cap * rows_total, 256);
+  p.o_bytes = round_up(part_elem * (size_t)p.items_cap * rows_total * mla::kVDim, 256);
+  return p;
+}
+
+mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_t shard_begin,
+                                int32_t shard_count, void* ws) {
+  mla::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.kv = static_cast<const uint16_t*>(a->kv_cache);
+  p.table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  char* w = static_cast<char*>(ws);
+  p.plan_out = reinterpret_cast<int32_t*>(w);
+  p.part_lse = reinterpret_cast<float*>(w + pl.plan_bytes);
+  p.part_o = w + pl.plan_bytes + pl.lse_bytes;
+  p.B = a->batch;
+  p.R = a->rows;
+  p.H = a->heads;
+  p.rows_total = a->rows * a->heads;
+  p.row_groups = pl.row_groups;
+  p.num_blocks = a->num_blocks;
+  p.bs_log2 = ilog2_exact(a->block_size);
+  p.max_blocks = a->max_blocks_per_seq;
+  p.cap_tokens = a->max_blocks_per_seq * a->block_size;
+  p.S = a->num_shards;
+  p.I = a->interleave;
+  p.shard_begin = shard_begin;
+  p.shard_count = shard_count;
+  p.pairs = pl.pairs;
+  p.items_cap = pl.items_cap;
+  p.tpi_min = pl.tpi_min;
+  p.tpi_max = pl.tpi_max;
+  p.c_log2 = a->softmax_scale * mla::kLog2e;
+  p.causal = a->causal ? 1 : 0;
+  return p;
+}
+
+int launch_partial(const mla::DecodeParams& p, hipStream_t stream, bool bf16) {
+  const int grid = p.row_groups == 1 ? p.items_cap : ceil_div(p.items_cap, 8) * 8 * p.row_groups;
+  if (bf16)
+    hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(grid), dim3(mla::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(mla::partial_kernel<false>, dim3(grid), dim3(mla::kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int launch_combine(const mla::CombineParams& c, int64_t units, hipStream_t stream, bool bf16) {
+  if (units * 4 > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  const int grid = (int)(units * 4);
+  if (bf16)
+    hipLaunchKernelGGL(mla::combine_kernel<true>, dim3(grid), dim3(mla::kThreads), 0, stream, c);
+  else
+    hipLaunchKernelGGL(mla::combine_kernel<false>, dim3(grid), dim3(mla::kThreads), 0, stream, c);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_workspace_bytes(const mla_decode_args* a) {
+  if (check_args(a) != MLA_OK) return 0;
+  return make_plan(a, 0, a->num_shards).total();
+}
+
+int32_t mla_plan_capacity(const mla_decode_args* a, int32_t shard_count, int32_t* row_groups) {
+  if (check_args(a) != MLA_OK || shard_count < 1 || shard_count > a->num_shards) return -1;
+  const Plan p = make_plan(a, 0, shard_count);
+  if (row_groups) *row_groups = p.row_groups;
+  return p.items_cap;
+}
+
+int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count,
+                             float* out_partial, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int st = check_args(a);
+  if (st != MLA_OK) return st;
+  if (shard_begin < 0 || shard_count < 1 || (int64_t)shard_begin + shard_count > a->num_shards)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch == 0) return MLA_OK;
+  if (!out_partial || !lse || !workspace) return MLA_ERR_INVALID_ARG;
+  const Plan pl = make_plan(a, shard_begin, shard_count);
+  if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = partials_in_bf16();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla::DecodeParams p = decode_params(a, pl, shard_begin, shard_count, workspace);
+  if ((st = launch_partial(p, s, bf16)) != MLA_OK) return st;
+  mla::CombineParams c{};
+  c.src_o = p.part_o;
+  c.src_lse = p.part_lse;
+  c.plan = p.plan_out;
+  c.seq_lens = a->seq_lens;
+  c.cap_tokens = p.cap_tokens;
+  c.items_cap = p.items_cap;
+  c.out = out_partial;
+  c.lse_shard = lse;
+  c.lse_final = nullptr;
+  c.B = a->batch;
+  c.rows = p.rows_total;
+  c.shard_count = shard_count;
+  c.mode = mla::kMergeShard;
+  return launch_combine(c, (int64_t)shard_count * a->batch * p.rows_total, s, bf16);
+}
+
+int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
+                    int32_t rows, int32_t heads, void* out, float* lse_final, void* stream) {
+  if (num_shards < 1 || batch < 0 || rows < 1 || heads < 1 || (int64_t)rows * heads > (1 << 20))
+    return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!out_partial || !lse || !out) return MLA_ERR_INVALID_ARG;
+  mla::CombineParams c{};
+  c.src_o = out_partial;
+  c.src_lse = lse;
+  c.plan = nullptr;
+  c.seq_lens = nullptr;
+  c.items_cap = 0;
+  c.out = out;
+  c.lse_shard = nullptr;
+  c.lse_final = lse_final;
+  c.B = batch;
+  c.rows = rows * heads;
+  c.shard_count = num_shards;
+  c.mode = mla::kCombineShards;
+  return launch_combine(c, (int64_t)batch * c.rows, static_cast<hipStream_t>(stream), false);
+}
+
+int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* workspace,
+                           size_t workspace_bytes, void* stream, void* ev_begin, void* ev_mid, void* ev_end) {
+  int st = check_args(a);
+  if (st != MLA_OK) return st;
+  if (a->batch == 0) return MLA_OK;
+  if (!out || !lse || !workspace) return MLA_ERR_INVALID_ARG;
+  const Plan pl = make_plan(a, 0, a->num_shards);
+  if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = partials_in_bf16();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla::DecodeParams p = decode_params(a, pl, 0, a->num_shards, workspace);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return MLA_ERR_HIP;
+  if ((st = launch_partial(p, s, bf16)) != MLA_OK) return st;
+  if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), s) != hipSuccess) return MLA_ERR_HIP;
+  mla::CombineParams c{};
+  c.src_o = p.part_o;
+  c.src_lse = p.part_lse;
+  c.plan = p.plan_out;
+  c.seq_lens = a->seq_lens;
+  c.cap_tokens = p.cap_tokens;
+  c.items_cap = p.items_cap;
+  c.out = out;
+  c.lse_shard = lse;
+  c.lse_final = lse_final;
+  c.B = a->batch;
+  c.rows = p.rows_total;
+  c.shard_count = a->num_shards;
+  c.mode = mla::kCombineItems;
+  if ((st = launch_combine(c, (int64_t)a->batch * p.rows_total, s, bf16)) != MLA_OK) return st;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return mla_split_decode_timed(a, out, lse, lse_final, workspace, workspace_bytes, stream, nullptr, nullptr,
+                                nullptr);
+}
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances: output |err| <= 2e-3 + 1e-2 |ref| elementwise; LSE |err| <= 1e-3;
+the -inf pattern of the per-shard LSE and the +0.0 output of empty rows are
+bit-exact.  Small cases compare every element; the full-size workloads compare
+sampled (request, head) rows that the oracle computes one by one.
+"""
+
+import math
+import zlib
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import build
+from tests.gpu_helpers import (assert_lse_close, assert_out_close, bf16_to_f64, to_device)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+def _lib():
+    import split_kv_mla_amd
+    split_kv_mla_amd.load_library()
+    return split_kv_mla_amd
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run_split(w, **kw):
+    m = _lib()
+    q, kv, bt, sl = to_device(w)
+    out, lse, lf = m.mla_split_decode(q, kv, bt, sl, w.num_shards, w.interleave, w.scale, w.causal, **kw)
+    torch.cuda.synchronize()
+    return bf16_to_f64(out), lse.cpu().double().numpy(), lf.cpu().double().numpy()
+
+
+def _check_full(w, tag):
+    _say(f"[parity] {tag}: B={w.B} R={w.R} H={w.H} S={w.num_shards} I={w.interleave} "
+         f"bs={w.block_size} lens={w.seq_lens.tolist()[:8]}")
+    out, lse, lf = _run_split(w)
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                   w.interleave, w.scale, w.causal, with_shards=False)
+    e_out = assert_out_close(out, ref["out"], what=f"{tag} out")
+    e_lse = assert_lse_close(lse, ref["lse_shard"], what=f"{tag} lse_shard")
+    e_lf = assert_lse_close(lf, ref["lse_final"], what=f"{tag} lse_final")
+    empty = np.isneginf(ref["lse_final"])
+    if empty.any():
+        z = out[empty]
+        assert np.all(z == 0.0) and not np.signbit(z).any(), f"{tag}: empty rows must be +0.0"
+    _say(f"[parity] {tag}: max err out {e_out:.2e} lse {e_lse:.2e} lse_final {e_lf:.2e}")
+
+
+SMALL = [
+    # name, lens, R, H, S, I, bs
+    ("one_tile", [7], 1, 16, 1, 1, 64),
+    ("ragged_tail", [1, 37, 300], 1, 32, 3, 1, 16),
+    ("many_tiles_h128", [2000, 513], 1, 128, 2, 1, 64),
+    ("shards8_i1_empty", [5, 3, 900], 1, 64, 8, 1, 64),
+    ("interleave16", [1000, 45], 1, 32, 8, 16, 64),
+    ("interleave3_bs32", [777], 1, 16, 5, 3, 32),
+    ("verify_r4_h32", [4, 100, 1000], 4, 32, 8, 16, 64),
+    ("verify_r4_h16_short", [1, 2, 3, 4], 4, 16, 2, 1, 16),
+    ("r2_h64", [129, 64], 2, 64, 4, 2, 128),
+    ("padding_rows", [300, 0, 17, 0], 1, 128, 8, 1, 64),
+    ("h24_rows_not_multiple", [90], 1, 24, 3, 1, 8),
+    ("bs1", [50], 1, 16, 2, 1, 1),
+    ("rows_512", [200], 4, 128, 2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, lens, R, H, S, I, bs = case
+    w = build(name, lens, R=R, H=H, num_shards=S, interleave=I, seed=zlib.crc32(name.encode()) % 1000, block_size=bs)
+    _check_full(w, name)
+
+
+def test_noncausal_verify_rows():
+    w = build("noncausal", [300, 5], R=3, H=32, num_shards=4, interleave=2, seed=77, causal=False)
+    _check_full(w, "noncausal")
+
+
+def test_outliers_and_large_q():
+    w = build("outliers", [1500, 64], R=1, H=64, num_shards=8, interleave=1, seed=78,
+              outlier_frac=0.01, q_scale=2.0)
+    _check_full(w, "outliers")
+
+
+def test_tiny_config():
+    _check_full(workloads.tiny(), "tiny_config")
+
+
+def test_shard_partial_matches_oracle():
+    w = build("partial", [400, 9, 0], R=2, H=32, num_shards=4, interleave=3, seed=31, block_size=16)
+    m = _lib()
+    q, kv, bt, sl = to_device(w)
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                   w.interleave, w.scale, w.causal)
+    for begin, count in [(0, 4), (1, 2), (3, 1)]:
+        _say(f"[parity] shard_partial begin={begin} count={count}")
+        op, lp = m.mla_shard_decode_partial(q, kv, bt, sl, w.num_shards, w.interleave, w.scale, w.causal,
+                                            shard_begin=begin, shard_count=count)
+        torch.cuda.synchronize()
+        op = op.cpu().double().numpy()
+        lp = lp.cpu().double().numpy()
+        rl = ref["lse_shard"][begin:begin + count]
+        ro = ref["out_shard"][begin:begin + count]
+        assert_lse_close(lp, rl, what="shard lse")
+        live = ~np.isneginf(rl)
+        assert_out_close(op, ro, mask=np.broadcast_to(live[..., None], ro.shape), what="shard out")
+
+
+def test_lse_combine_skips_empty_sources():
+    """Empty sources carry NaN payloads; the combine must never read them."""
+    w = build("combine", [300, 5, 0], R=1, H=16, num_shards=8, interleave=1, seed=32, block_size=16)
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                   w.interleave, w.scale, w.causal)
+    po = ref["out_shard"].copy()
+    po[np.isneginf(ref["lse_shard"])] = np.nan
+    m = _lib()
+    op = torch.from_numpy(po.astype(np.float32)).cuda()
+    lp = torch.from_numpy(ref["lse_shard"].astype(np.float32)).cuda()
+    _say("[parity] lse_combine with NaN payloads in empty sources")
+    out, lf = m.mla_lse_combine(op, lp)
+    torch.cuda.synchronize()
+    out = bf16_to_f64(out)
+    lf = lf.cpu().double().numpy()
+    eo, el = oracle.lse_combine_oracle(po, ref["lse_shard"])
+    assert_out_close(out, eo, what="combine out")
+    assert_lse_close(lf, el, what="combine lse")
+    assert np.all(out[2] == 0.0) and not np.signbit(out[2]).any()
+
+
+def test_repeat_runs_bitwise_identical():
+    w = build("det", [3000, 700], R=1, H=128, num_shards=8, interleave=1, seed=33)
+    a = _run_split(w)
+    b = _run_split(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_block_permutation_bitwise_identical():
+    w = build("perm", [1000, 250], R=2, H=64, num_shards=4, interleave=2, seed=34, block_size=32)
+    a = _run_split(w)
+    rng = np.random.default_rng(35)
+    p = np.concatenate([[0], rng.permutation(w.num_blocks - 1) + 1])
+    kv2 = np.empty_like(w.kv_bits)
+    kv2[p] = w.kv_bits
+    w.kv_bits = kv2
+    w.block_table = p[w.block_table].astype(np.int32)
+    b = _run_split(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_bad_block_id_poisons_only_its_request():
+    w = build("badblk", [200, 200], R=1, H=16, num_shards=2, interleave=1, seed=36, block_size=16)
+    w.block_table[1, 3] = w.num_blocks + 5  # out of range
+    out, lse, lf = _run_split(w)
+    assert np.isnan(out[1]).all() and np.isnan(lf[1]).all()
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, 2, 1, w.scale, True,
+                                   requests=[0], with_shards=False)
+    assert_out_close(out[0], ref["out"][0])
+    assert_lse_close(lf[0], ref["lse_final"][0])
+
+
+def test_seq_len_beyond_table_is_nan():
+    w = build("badlen", [100, 60], R=1, H=16, num_shards=2, interleave=1, seed=37, block_size=16,
+              max_blocks=8)
+    w.seq_lens[1] = 8 * 16 + 1
+    out, lse, lf = _run_split(w)
+    assert np.isnan(out[1]).all() and np.isnan(lf[1]).all() and np.isnan(lse[:, 1]).all()
+    assert np.isfinite(out[0]).all()
+
+
+def test_batch_zero_is_noop():
+    m = _lib()
+    q = torch.empty((0, 1, 16, 576), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 64, 576), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    sl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out, lse, lf = m.mla_split_decode(q, kv, bt, sl, 2, 1, SCALE)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 1, 16, 512)
+
+
+# ------------------------------------------------------------ full workloads
+
+def _sampled_parity(w, requests, heads, tag):
+    _say(f"[parity] {tag}: upload and run, B={w.B} R={w.R} H={w.H} sum_len={int(w.seq_lens.sum())}")
+    out, lse, lf = _run_split(w)
+    _say(f"[parity] {tag}: oracle on requests {requests} heads {heads}")
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                   w.interleave, w.scale, w.causal, requests=requests, heads=heads,
+                                   with_shards=False)
+    ob = out[requests][:, :, heads]
+    rb = ref["out"][requests][:, :, heads]
+    e1 = assert_out_close(ob, rb, what=f"{tag} out")
+    e2 = assert_lse_close(lse[:, requests][:, :, :, heads], ref["lse_shard"][:, requests][:, :, :, heads],
+                          what=f"{tag} lse_shard")
+    e3 = assert_lse_close(lf[requests][:, :, heads], ref["lse_final"][requests][:, :, heads],
+                          what=f"{tag} lse_final")
+    _say(f"[parity] {tag}: max err out {e1:.2e} lse {e2:.2e} lse_final {e3:.2e}")
+    # properties that hold at any size for every row: finite outputs where the
+    # row has tokens, +0 / -inf where it has none, shard -inf pattern exact
+    R = w.R
+    for b in range(w.B):
+        for r in range(R):
+            n = max(int(w.seq_lens[b]) - (R - 1 - r), 0) if w.causal else int(w.seq_lens[b])
+            for s in range(w.num_shards):
+                has = n > s * w.interleave  # the shard's first token is global position s * I
+                assert np.isneginf(lse[s, b, r]).all() == (not has)
+                assert np.isfinite(lse[s, b, r]).all() == has
+            if n == 0:
+                assert np.all(out[b, r] == 0.0) and np.isneginf(lf[b, r]).all()
+            else:
+                assert np.isfinite(out[b, r]).all() and np.isfinite(lf[b, r]).all()
+    return out, lse, lf
+
+
+def test_batch_decode_config():
+    w = workloads.batch_decode()
+    short = int(np.nonzero(w.seq_lens == 5)[0][0])
+    _sampled_parity(w, [short, (short + 1) % 8, (short + 5) % 8], [0, 37, 127], "batch_decode")
+
+
+def test_long_context_config():
+    w = workloads.long_context(1)
+    _sampled_parity(w, [0], [0, 1, 63, 127], "long120k_b1")
+
+
+def test_long_context_b2_shared_prefix():
+    w = workloads.long_context(2)
+    out, _, _ = _sampled_parity(w, [0, 1], [5, 100], "long120k_b2")
+
+
+def test_verify_config():
+    w = workloads.verify()
+    _sampled_parity(w, [0, 7], [3, 64], "verify_r4")
+
+
+def test_padded_config():
+    w = workloads.padded()
+    order = np.argsort(w.seq_lens[:56])
+    picks = [int(order[0]), int(order[28]), int(order[-1]), 60]
+    _sampled_parity(w, picks, [0, 99], "padded_b64")
