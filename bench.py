@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
+    ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--min-kv-set-mb", type=float, default=640.0,
                     help="cycle KV copies until the cycled set exceeds this many MB")
     return ap.parse_args()
@@ -89,9 +91,16 @@ def main():
     import workloads
 
     mla.load_library()
-    w = workloads.STANDARD[args.workload]()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy_mb > 0:
+        n = int(args.calibrate_copy_mb * (1 << 20)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    w = workloads.STANDARD[args.workload]()
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)

@@ -50,6 +50,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
 constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
 constexpr int kRowsPerGroup = 4 * kRowsPerWave;   // 128 query rows per workgroup
+constexpr int kNumCUs = 256;                      // MI355X compute units: the persistent grid
+constexpr int kPlanPairsLds = 1024;               // per-pair item starts kept in LDS
+constexpr int kTilesPerWave = 128;                // per-CU tile walks that justify one more item wave
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -64,7 +67,9 @@ struct DecodeParams {
   int32_t B, R, H, rows_total, row_groups;
   int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
   int32_t S, I, shard_begin, shard_count, pairs;
+  int32_t i_log2;            // log2(I) when I is a power of two, else -1
   int32_t items_cap, tpi_min, tpi_max;
+  int32_t slots_per_wave;    // work units one wave of workgroups holds per row group
   float c_log2;              // softmax_scale * log2(e)
   int32_t causal;
 };
@@ -120,45 +125,123 @@ __device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
   return ceil_div(local_len(L, p.S, p.I, s), kTile);
 }
 
-struct ItemInfo {
-  int pair;   // -1: no work for this item slot
-  int k;      // item index within its pair
-  int tpi;    // tiles per item
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) t += scratch[i];
+  return t;
+}
+
+struct Plan {
+  int tpi;      // tiles per item
+  int n_items;  // items of the launch (per row group)
 };
 
-// Every workgroup computes the same plan; workgroup 0 also publishes it.
-__device__ ItemInfo locate_item(const DecodeParams& p, int item, int* scratch) {
-  int total = 0;
-  for (int base = 0; base < p.pairs; base += kThreads) {
-    const int pr = base + (int)threadIdx.x;
-    const int t = pr < p.pairs ? pair_tiles(p, pr) : 0;
-    int tot;
-    block_excl_scan(t, scratch, &tot);
-    total += tot;
-  }
-  const int tpi = tiles_per_item(total, p.items_cap, p.pairs, p.tpi_min, p.tpi_max);
-  if (threadIdx.x == 0) { scratch[8] = -1; scratch[9] = 0; }
-  int start = 0;
-  const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
-  for (int base = 0; base < p.pairs; base += kThreads) {
-    const int pr = base + (int)threadIdx.x;
-    const int t = pr < p.pairs ? pair_tiles(p, pr) : 0;
-    const int cnt = ceil_div(t, tpi);
-    int tot;
-    const int my0 = start + block_excl_scan(cnt, scratch, &tot);
-    if (pr < p.pairs) {
-      if (publish) p.plan_out[pr] = my0;
-      if (item >= my0 && item < my0 + cnt) { scratch[8] = pr; scratch[9] = item - my0; }
+// The split of every (request, shard) pair's tiles into items, identical in
+// every workgroup.  Items per row group aim at W waves of the grid (W from the
+// total work); pairs with tokens each take at least one item.  Item starts per
+// pair go to `starts` (LDS) when the pairs fit, and workgroup 0 publishes them
+// with the item total and tiles-per-item for the combine.
+__device__ Plan make_plan(const DecodeParams& p, int* starts, int* scratch) {
+  const int P = p.pairs;
+  const bool in_reg = P <= kThreads;
+  const int my_t = (in_reg && (int)threadIdx.x < P) ? pair_tiles(p, threadIdx.x) : 0;
+  auto pair_sum = [&](auto f) -> int {
+    if (in_reg) return block_sum(f(my_t), scratch);
+    int tot = 0;
+    for (int base = 0; base < P; base += kThreads) {
+      const int pr = base + (int)threadIdx.x;
+      tot += block_sum(pr < P ? f(pair_tiles(p, pr)) : 0, scratch);
     }
-    start += tot;
+    return tot;
+  };
+  const int T = pair_sum([](int t) { return t; });
+  const int nonempty = pair_sum([](int t) { return t > 0 ? 1 : 0; });
+  const int64_t walks = (int64_t)T * p.row_groups;
+  int W = (int)((walks + (int64_t)kNumCUs * kTilesPerWave - 1) / ((int64_t)kNumCUs * kTilesPerWave));
+  W = W < 1 ? 1 : (W > 4 ? 4 : W);
+  const int base = p.slots_per_wave * W;
+  const bool many_pairs = nonempty > base / 2;
+  const int target = min(many_pairs ? nonempty + base : base, p.items_cap);
+  const int free_slots = max(1, target - (many_pairs ? nonempty : 0));
+  int tpi = min(p.tpi_max, max(p.tpi_min, ceil_div(max(T, 1), free_slots)));
+  int n = 0;
+  for (int it = 0;; ++it) {
+    const int t_cur = tpi;
+    n = pair_sum([t_cur](int t) { return ceil_div(t, t_cur); });
+    if (n <= target || tpi >= p.tpi_max || it >= 6) break;
+    tpi = min(p.tpi_max, max(tpi + 1, (int)(((int64_t)tpi * n + target - 1) / target)));
   }
-  if (publish && threadIdx.x == 0) { p.plan_out[p.pairs] = start; p.plan_out[p.pairs + 1] = tpi; }
+  if (n > p.items_cap) {  // never exceed the slots the host sized for
+    tpi = p.tpi_max;
+    const int t_cur = tpi;
+    n = pair_sum([t_cur](int t) { return ceil_div(t, t_cur); });
+  }
+  const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
+  if (P <= kPlanPairsLds || publish) {
+    int run = 0;
+    for (int b0 = 0; b0 < P; b0 += kThreads) {
+      const int pr = b0 + (int)threadIdx.x;
+      const int t = in_reg ? my_t : (pr < P ? pair_tiles(p, pr) : 0);
+      const int cnt = pr < P ? ceil_div(t, tpi) : 0;
+      int tot;
+      const int ex = block_excl_scan(cnt, scratch, &tot);
+      if (pr < P) {
+        if (P <= kPlanPairsLds) starts[pr] = run + ex;
+        if (publish) p.plan_out[pr] = run + ex;
+      }
+      run += tot;
+    }
+    if (threadIdx.x == 0) {
+      if (P <= kPlanPairsLds) starts[P] = run;
+      if (publish) { p.plan_out[P] = run; p.plan_out[P + 1] = tpi; }
+    }
+  }
   __syncthreads();
-  ItemInfo info;
-  info.pair = scratch[8];
-  info.k = scratch[9];
-  info.tpi = tpi;
-  return info;
+  return Plan{tpi, n};
+}
+
+// Pair holding `item` and the item's first item index within that pair.
+__device__ int2 find_pair(const DecodeParams& p, const Plan& pl, int item, const int* starts, int* scratch) {
+  const int P = p.pairs;
+  if (P <= kPlanPairsLds) {
+    int lo = 0, hi = P;  // largest pr with starts[pr] <= item
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (starts[mid] <= item) lo = mid; else hi = mid;
+    }
+    while (lo + 1 < P && starts[lo + 1] <= item) ++lo;  // skip pairs without items
+    return make_int2(lo, starts[lo]);
+  }
+  // many pairs: scan the item counts again
+  int run = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) { scratch[8] = -1; scratch[9] = 0; }
+  for (int b0 = 0; b0 < P; b0 += kThreads) {
+    const int pr = b0 + (int)threadIdx.x;
+    const int cnt = pr < P ? ceil_div(pair_tiles(p, pr), pl.tpi) : 0;
+    int tot;
+    const int my0 = run + block_excl_scan(cnt, scratch, &tot);
+    if (pr < P && item >= my0 && item < my0 + cnt) { scratch[8] = pr; scratch[9] = my0; }
+    run += tot;
+  }
+  __syncthreads();
+  return make_int2(scratch[8], scratch[9]);
+}
+
+// XOR key of token tau's 16-byte pieces inside each 128-byte group of its LDS
+// row: a 3-bit rotation of tau / 2.  It keeps both LDS read patterns free of
+// bank conflicts (64 banks x 4 bytes): 16 consecutive tokens reading the same
+// piece (ds_read_b128 of the K operand) and 4 consecutive tokens x 32 bytes
+// per 16-lane group (ds_read_b64_tr_b16 of the V operand).
+__device__ __forceinline__ int piece_swizzle(int tau) {
+  const int y = (tau >> 1) & 7;
+  return ((y & 1) << 2) | (y >> 1);
 }
 
 template <int N>
@@ -167,6 +250,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes LDS
+// bytes [lds_base + 16 i, +16).  Issued as inline assembly so the compiler
+// neither counts it nor inserts waits for it: the LDS ring's explicit vmcnt
+// waits and barriers are what order these writes against the LDS reads.
+// M0 carries the LDS base; these kernels use M0 nowhere else, so clobbering
+// the reserved register is safe (a codegen test checks the assembly).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gaddr), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -185,6 +287,7 @@ template <bool kBf16Part>
 __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
   __shared__ int tbl[kTableCache];
+  __shared__ int starts[kPlanPairsLds + 1];
   __shared__ int scratch[16];
 
   const int tid = threadIdx.x;
@@ -192,88 +295,22 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const int lane = tid & 63;
   const int g = lane >> 5;      // which half of the wavefront
   const int l32 = lane & 31;
-
-  // Item and row group.  With several row groups, the groups of one item get
-  // block ids congruent mod 8, i.e. the same XCD and its L2.
-  int item, rg;
-  if (p.row_groups == 1) {
-    item = blockIdx.x;
-    rg = 0;
-  } else {
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    rg = k % p.row_groups;
-    item = (k / p.row_groups) * 8 + x;
-  }
-  if (item >= p.items_cap) return;
-
-  const ItemInfo info = locate_item(p, item, scratch);
-  if (info.pair < 0) return;
-  const int b = info.pair / p.shard_count;
-  const int s = p.shard_begin + info.pair % p.shard_count;
   const int S = p.S, I = p.I;
-  const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
-  const int n_bs = local_len(L, S, I, s);
-  const int tile0 = info.k * info.tpi;
-  const int tile1 = min(tile0 + info.tpi, ceil_div(n_bs, kTile));
-  const int nt = tile1 - tile0;
   const int bs_mask = (1 << p.bs_log2) - 1;
+  const float c = p.c_log2;
 
-  // Block-table window of this item (fits kTableCache by the choice of tpi_max).
-  const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
-  const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
-  const int span = blk_hi - blk_lo + 1;
-  bool bad = false;
-  for (int i = tid; i < span; i += kThreads) {
-    int v = p.table[(size_t)b * p.max_blocks + blk_lo + i];
-    if ((unsigned)v >= (unsigned)p.num_blocks) { v = 0; bad = true; }
-    tbl[i] = v;
-  }
+  const Plan pl = make_plan(p, starts, scratch);
+  const int G = p.row_groups;
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
 
-  // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
-  const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
-  const bool row_ok = row < p.rows_total;
-  const int r = row_ok ? row / p.H : 0;
-  const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
-  const int lim_min = wave_min(lim);
-
-  // Q^T operand: lane holds row l32, columns 16*db + 8*g .. +7 for db < 36.
-  bf16x8 qf[36];
-  {
-    const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + (row_ok ? row : 0)) * kHeadDim + 8 * g;
-#pragma unroll
-    for (int db = 0; db < 36; ++db) {
-      if (row_ok)
-        qf[db] = *reinterpret_cast<const bf16x8*>(qrow + 16 * db);
-      else
-        qf[db] = bf16x8{};
-    }
-  }
-  bad = __syncthreads_or(bad);
-  // Q must be resident before the LDS ring starts counting loads.
-#pragma unroll
-  for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
-  wait_vmcnt<0>();
-
+  // Per-lane LDS offsets (independent of the item).
   // DMA role: lane loads token tau of each tile, 16-byte pieces (lane & 7) ^ swz
   // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
-  //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ ((tau >> 1) & 7))
+  //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau))
   const int dma_tau = wave * 8 + (lane >> 3);
-  const int dma_swz = ((lane & 7) ^ ((dma_tau >> 1) & 7)) * 16;
-  auto issue_tile = [&](int kk, int stage) {
-    int j = kk * kTile + dma_tau;
-    j = j < n_bs ? j : n_bs - 1;  // rows past the end re-read the last valid row (masked later)
-    const int t = global_pos(j, S, I, s);
-    const int phys = tbl[(t >> p.bs_log2) - blk_lo];
-    const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
-    const char* src = reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
-    char* dst = ring + stage * kTileBytes + wave * 9 * 1024;
-#pragma unroll
-    for (int i = 0; i < 9; ++i)
-      __builtin_amdgcn_global_load_lds(src + 128 * i, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
-  };
-
+  const int dma_swz = ((lane & 7) ^ piece_swizzle(dma_tau)) * 16;
   // K-read (A of S^T = K Q^T): lane reads token l32, piece 2*db + g.
-  const int kswz = (l32 >> 1) & 7;
+  const int kswz = piece_swizzle(l32);
   const int kbase = (576 * (l32 >> 3) + 8 * (l32 & 7)) * 16;
   int koff[4];
 #pragma unroll
@@ -283,8 +320,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const int h16 = (lane >> 4) & 1;
   const int rr = (lane & 15) >> 2;
   const int cc = lane & 3;
-  const int f1 = (2 * g + (rr >> 1)) & 7;
-  const int f2 = (4 + 2 * g + (rr >> 1)) & 7;
+  const int f1 = piece_swizzle(4 * g + rr);      // tokens 16*kb + 4g + rr
+  const int f2 = piece_swizzle(8 + 4 * g + rr);  // tokens 16*kb + 8 + 4g + rr
   int voff1[2], voff2[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -293,151 +330,273 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     voff2[e] = 9216 + 128 * (4 * g + rr) + 16 * (pc ^ f2) + 8 * (cc & 1);
   }
 
-  f32x16 acc[16];
-  float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
-  float l_run = 0.f;
-  const float c = p.c_log2;
-
-  // One pipelined walk over the item's tiles.  kMaxOnly: only the exact row
-  // maximum of the scores (written to m_ref).  Otherwise the softmax
-  // numerator and denominator against m_ref; m_ref is taken from the first
-  // tile that holds a token of the row, and a later tile whose maximum exceeds
-  // it by more than kSlack (a possible fp32 overflow of the sums) sets
-  // `overflow` instead of rescaling the accumulators.
-  constexpr float kSlack = 64.f;
-  auto walk = [&](auto max_only_tag, bool& overflow) {
-    constexpr bool kMaxOnly = decltype(max_only_tag)::value;
-    const int pre = min(nt, kStages - 1);
-    for (int k = 0; k < pre; ++k) issue_tile(tile0 + k, k);
-    float m_walk = -INFINITY;
-    for (int k = 0; k < nt; ++k) {
-      // tile k resident: at most min(nt-1-k, kStages-2) younger tiles in flight
-      const int younger = min(nt - 1 - k, kStages - 2);
-      if (younger >= 2) wait_vmcnt<18>();
-      else if (younger == 1) wait_vmcnt<9>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (k + kStages - 1 < nt) issue_tile(tile0 + k + kStages - 1, (k + kStages - 1) % kStages);
-      const char* buf = ring + (k % kStages) * kTileBytes;
-
-      // S^T[token][row] for 32 tokens x 32 rows.
-      f32x16 sc = f32x16{};
-#pragma unroll
-      for (int db = 0; db < 36; ++db) {
-        if ((db & 3) == 0) asm volatile("" ::: "memory");  // bound how far LDS reads run ahead
-        const bf16x8 a = lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[db], sc, 0, 0, 0);
-      }
-      // lane holds row l32 and tokens 8*(i/4) + 4*g + (i%4)
-      const int jt = (tile0 + k) * kTile;
-      if (jt + kTile > lim_min) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = jt + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (j >= lim) sc[i] = -INFINITY;
-        }
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-      if constexpr (kMaxOnly) {
-        m_walk = fmaxf(m_walk, mx);
-        continue;
-      } else {
-        if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet: no rescale needed
-        overflow |= mx > m_ref + kSlack;
-        const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
-        float pv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -msafe));
-          l_run += pv[i];
-        }
-        // P = P_hi + P_lo, both bf16: a single bf16 P would cost up to 2^-8 of
-        // relative weight per token, too much for rows of a few tokens or with
-        // outlier values; the pair leaves a residual of at most 2^-16 p.
-        bf16x8 pb[2], pl[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float x = pv[8 * kb + j];
-            const __bf16 hi = (__bf16)x;
-            pb[kb][j] = hi;
-            pl[kb][j] = (__bf16)(x - (float)hi);
-          }
-
-        // O^T[dim][row] += V^T[dim][token] P^T[token][row]
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int db = 0; db < 16; ++db) {
-            if ((db & 3) == 0) asm volatile("" ::: "memory");
-            const int off = 18432 * kb + 1024 * (db >> 1);
-            const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
-            const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], acc[db], 0, 0, 0);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl[kb], acc[db], 0, 0, 0);
-          }
-        }
-      }
+  // Work units = (item, row group), walked by the persistent grid.  The row
+  // groups of one item get unit ids congruent mod 8, and unit u runs on
+  // workgroup u mod gridDim (a multiple of 8): the same XCD and its L2.
+  const int units = ceil_div(pl.n_items, 8) * 8 * G;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    int item, rg;
+    if (G == 1) {
+      item = u;
+      rg = 0;
+    } else {
+      const int x = u & 7, k8 = u >> 3;
+      rg = k8 % G;
+      item = (k8 / G) * 8 + x;
     }
-    if constexpr (kMaxOnly) m_ref = m_walk;
-  };
+    if (item >= pl.n_items) continue;
+    const int2 pk = find_pair(p, pl, item, starts, scratch);
+    const int pair = pk.x;
+    const int b = pair / p.shard_count;
+    const int s = p.shard_begin + pair % p.shard_count;
+    const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
+    const int n_bs = local_len(L, S, I, s);
+    const int tile0 = (item - pk.y) * pl.tpi;
+    const int tile1 = min(tile0 + pl.tpi, ceil_div(n_bs, kTile));
+    const int nt = tile1 - tile0;
 
-  using MaxOnly = std::integral_constant<bool, true>;
-  using Full = std::integral_constant<bool, false>;
-#pragma unroll
-  for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
-  bool overflow = false;
-  walk(Full{}, overflow);
-  if (__syncthreads_or(overflow)) {
-    // Rare slow path: scores grew by more than 2^64 after the reference was
-    // fixed.  Find each row's exact maximum, then redo the walk against it.
-    bool unused = false;
-    walk(MaxOnly{}, unused);
+    // The previous unit is done with the ring and the table window.
     __syncthreads();
+
+    // Block-table window of this item (fits kTableCache by the choice of tpi_max).
+    const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
+    const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
+    const int span = blk_hi - blk_lo + 1;
+    bool bad = false;
+    for (int i = tid; i < span; i += kThreads) {
+      int v = p.table[(size_t)b * p.max_blocks + blk_lo + i];
+      if ((unsigned)v >= (unsigned)p.num_blocks) { v = 0; bad = true; }
+      tbl[i] = v;
+    }
+    bad = __syncthreads_or(bad);
+
+    // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
+    const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
+    const bool row_ok = row < p.rows_total;
+    const int r = row_ok ? row / p.H : 0;
+    const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
+    const int lim_min = wave_min(lim);
+
+    // Tile kk of the pair into ring stage `stage`; tiles at or past nt re-read
+    // the item's last tile (the prologue's spare stages).
+    auto issue_tile = [&](int kk, int stage) {
+      kk = min(kk, tile1 - 1);
+      int j = kk * kTile + dma_tau;
+      j = j < n_bs ? j : n_bs - 1;  // rows past the end re-read the last valid row (masked later)
+      // global position of local token j (shifts when I is a power of two)
+      const int t = p.i_log2 >= 0 ? (((j >> p.i_log2) * S + s) << p.i_log2) | (j & (I - 1))
+                                  : global_pos(j, S, I, s);
+      const int phys = tbl[(t >> p.bs_log2) - blk_lo];
+      const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
+      const char* src = reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds_ring + (uint32_t)(stage * kTileBytes + wave * 9 * 1024));
+#pragma unroll
+      for (int i = 0; i < 9; ++i) dma16(src + 128 * i, dst + 1024 * i);
+    };
+
+    // Prologue: tile 0, then Q (lane holds row l32, columns 16*db + 8*g .. +7)
+    // under the first tile's latency, then tiles 1 and 2.  Rows past
+    // rows_total load row 0 and never write.
+    issue_tile(tile0, 0);
+    bf16x8 qf[36];
+    {
+      const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + (row_ok ? row : 0)) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qrow + 16 * db);
+    }
+#pragma unroll
+    for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
+    issue_tile(tile0 + 1, 1);
+    issue_tile(tile0 + 2, 2);
+
+    f32x16 acc[16];
+    float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
+    float l_run = 0.f;
+
+    // One pipelined walk over the item's tiles.  kMaxOnly: only the exact row
+    // maximum of the scores (written to m_ref).  Otherwise the softmax
+    // numerator and denominator against m_ref; m_ref is taken from the first
+    // tile that holds a token of the row, and if the denominator ends above
+    // 2^96 (some score exceeded the reference enough to endanger the fp32
+    // sums) the walk sets `overflow` instead of rescaling the accumulators.
+    constexpr float kSlackValue = 7.9228162514264337593543950336e28f;  // 2^96
+    auto walk = [&](auto max_only_tag, bool prologue_issued, bool& overflow) {
+      constexpr bool kMaxOnly = decltype(max_only_tag)::value;
+      if (!prologue_issued)
+        for (int k = 0; k < kStages - 1; ++k) issue_tile(tile0 + k, k);
+      float m_walk = -INFINITY;
+      for (int k = 0; k < nt; ++k) {
+        // tile k resident: the prologue always fills kStages-1 stages, so the
+        // younger loads in flight are min(2, nt-1-k), or the spare re-reads
+        // when the item has fewer than kStages-1 tiles
+        const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
+        if (younger >= 2) wait_vmcnt<18>();
+        else if (younger == 1) wait_vmcnt<9>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        const char* buf = ring + (k % kStages) * kTileBytes;
+
+        // S^T[token][row] for 32 tokens x 32 rows; LDS reads run kQkAhead MFMAs ahead.
+        f32x16 sc = f32x16{};
+        {
+          bf16x8 kf[36];
+#pragma unroll
+          for (int db = 0; db < 36; ++db) kf[db] = lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+#pragma unroll
+          for (int db = 0; db < 36; ++db) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[db], qf[db], sc, 0, 0, 0);
+          constexpr int kQkAhead = 6;
+          __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
+#pragma unroll
+          for (int i = 0; i < 36 - kQkAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
+        }
+        // Refill the stage freed by the previous tile while the score block drains
+        // out of the matrix pipe.
+        if (k + kStages - 1 < nt) issue_tile(tile0 + k + kStages - 1, (k + kStages - 1) % kStages);
+        // lane holds row l32 and tokens 8*(i/4) + 4*g + (i%4)
+        const int jt = (tile0 + k) * kTile;
+        if (jt + kTile > lim_min) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = jt + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (j >= lim) sc[i] = -INFINITY;
+          }
+        }
+        if constexpr (kMaxOnly) {
+          float mx = sc[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+          m_walk = fmaxf(m_walk, fmaxf(mx, __shfl_xor(mx, 32, 64)) * c);
+        } else {
+          // The first tile that holds a token of the row fixes the reference
+          // (nothing has been accumulated yet, so nothing is rescaled).
+          if (__any(m_ref == -INFINITY)) {
+            float mx = sc[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+            if (m_ref == -INFINITY) m_ref = mx;
+          }
+          const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
+          // P = P_hi + P_lo, both bf16: a single bf16 P would cost up to 2^-8 of
+          // relative weight per token, too much for rows of a few tokens or with
+          // outlier values; the pair leaves a residual of at most 2^-16 p.
+          // The second half of the tile's P is formed under the first half's MFMAs.
+          bf16x8 pb[2], pl[2];
+          auto make_p = [&](int kb) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
+              l_run += x;
+              const __bf16 hi = (__bf16)x;
+              pb[kb][j] = hi;
+              pl[kb][j] = (__bf16)(x - (float)hi);
+            }
+          };
+          make_p(0);
+
+          // O^T[dim][row] += V^T[dim][token] P^T[token][row]; the two transposing
+          // reads of a V fragment run kPvAhead fragments ahead of their MFMAs.
+          {
+            bf16x8 vf[32];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int db = 0; db < 16; ++db) {
+                const int off = 18432 * kb + 1024 * (db >> 1);
+                const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
+                const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
+                vf[16 * kb + db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              if (kb == 1) make_p(1);
+#pragma unroll
+              for (int db = 0; db < 16; ++db) {
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[16 * kb + db], pb[kb], acc[db], 0, 0, 0);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[16 * kb + db], pl[kb], acc[db], 0, 0, 0);
+              }
+            }
+            constexpr int kPvAhead = 3;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 0);
+#pragma unroll
+            for (int i = 0; i < 32 - kPvAhead; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPvAhead, 0);
+          }
+        }
+      }
+      if constexpr (kMaxOnly) {
+        m_ref = m_walk;
+      } else {
+        // a score far above the reference pushes the denominator past 2^96 (or to
+        // inf/NaN): then the walk is redone from the exact maximum
+        overflow |= !(l_run < kSlackValue);
+      }
+      if constexpr (kMaxOnly) m_ref = m_walk;
+    };
+
+    using MaxOnly = std::integral_constant<bool, true>;
+    using Full = std::integral_constant<bool, false>;
 #pragma unroll
     for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
-    l_run = 0.f;
-    const float m_exact = m_ref;
-    walk(Full{}, unused);
-    m_ref = m_exact;
-  }
+    bool overflow = false;
+    walk(Full{}, true, overflow);
+    wait_vmcnt<0>();  // spare prologue re-reads of short items
+    if (__syncthreads_or(overflow)) {
+      // Rare slow path: scores grew by more than 2^64 after the reference was
+      // fixed.  Find each row's exact maximum, then redo the walk against it.
+      bool unused = false;
+      walk(MaxOnly{}, false, unused);
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
+      l_run = 0.f;
+      const float m_exact = m_ref;
+      walk(Full{}, false, unused);
+      wait_vmcnt<0>();
+      m_ref = m_exact;
+    }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (!row_ok) return;
-  const size_t prow = (size_t)item * p.rows_total + row;
-  float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  if (bad) lse = __builtin_nanf("");
-  if (g == 0) p.part_lse[prow] = lse;
-  if (!(l_tot > 0.f)) return;
-  const float inv = 1.f / l_tot;
-  // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3]
-  if constexpr (kBf16Part) {
-    __bf16* po = reinterpret_cast<__bf16*>(p.part_o) + prow * kVDim + 4 * g;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!row_ok) continue;
+    const size_t prow = (size_t)item * p.rows_total + row;
+    float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    if (bad) lse = __builtin_nanf("");
+    if (g == 0) p.part_lse[prow] = lse;
+    if (!(l_tot > 0.f)) continue;
+    const float inv = 1.f / l_tot;
+    // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3]
+    if constexpr (kBf16Part) {
+      __bf16* po = reinterpret_cast<__bf16*>(p.part_o) + prow * kVDim + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
+      for (int db = 0; db < 16; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 v;
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * q + e] * inv);
-        *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * q) = v;
-      }
-  } else {
-    float* po = reinterpret_cast<float*>(p.part_o) + prow * kVDim + 4 * g;
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * q + e] * inv);
+          *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * q) = v;
+        }
+    } else {
+      float* po = reinterpret_cast<float*>(p.part_o) + prow * kVDim + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
+      for (int db = 0; db < 16; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q) = v;
-      }
+          for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q) = v;
+        }
+    }
   }
 }
 
@@ -482,9 +641,14 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) 
   return r;
 }
 
+constexpr int kCombineCols = 128;             // output columns per workgroup
+constexpr int kCombineGroups = 16;            // source groups per workgroup
+constexpr int kCombineLdsSources = 2048;      // source LSEs staged in LDS
+
 template <bool kBf16Part>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  __shared__ f32x4 part[8][32];
+  __shared__ float src_lse[kCombineLdsSources];
+  __shared__ f32x4 part[kCombineGroups][kCombineCols / 4];
   __shared__ float red[8];
 
   const int tid = threadIdx.x;
@@ -523,60 +687,75 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     const int32_t L = p.seq_lens[b];
     bad = bad || L < 0 || L > p.cap_tokens;
   }
+  const int n = i1 - i0;
+  const bool staged = n <= kCombineLdsSources;
+  auto lse_of = [&](int i) -> float {  // i relative to i0
+    return staged ? src_lse[i] : p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
+  };
 
-  // pass 1: max and total weight
+  // pass 1: stage the source LSEs, their max, and the total weight
   float m = -INFINITY;
-  for (int i = i0 + tid; i < i1; i += kThreads) m = nan_max(m, p.src_lse[l_base + (size_t)i * l_stride]);
-  m = block_reduce(m, true, red);
+  for (int i = tid; i < n; i += kThreads) {
+    const float x = p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
+    if (staged) src_lse[i] = x;
+    m = nan_max(m, x);
+  }
+  m = block_reduce(m, true, red);  // its barriers also publish src_lse
   bad = bad || (m != m);
   const bool empty = (m == -INFINITY);
   float wsum = 0.f;
   if (!bad && !empty)
-    for (int i = i0 + tid; i < i1; i += kThreads) {
-      const float x = p.src_lse[l_base + (size_t)i * l_stride];
+    for (int i = tid; i < n; i += kThreads) {
+      const float x = lse_of(i);
       if (x != -INFINITY) wsum += __builtin_amdgcn_exp2f((x - m) * kLog2e);
     }
   wsum = block_reduce(wsum, false, red);
 
-  // pass 2: weighted sum of this block's 128 columns
-  const int sg = tid >> 5;        // source group
-  const int col = quarter * 128 + 4 * (tid & 31);
-  f32x4 acc = f32x4{};
+  // pass 2: weighted sum of this block's 128 columns; thread = (source group, 8 columns)
+  const int sg = tid >> 4;
+  const int col = quarter * kCombineCols + 8 * (tid & 15);
+  f32x4 acc0 = f32x4{}, acc1 = f32x4{};
   if (!bad && !empty) {
-    for (int i = i0 + sg; i < i1; i += 8) {
-      const float x = p.src_lse[l_base + (size_t)i * l_stride];
+#pragma unroll 4
+    for (int i = sg; i < n; i += kCombineGroups) {
+      const float x = lse_of(i);
       if (x == -INFINITY) continue;  // empty source: its payload is never read
       const float w = __builtin_amdgcn_exp2f((x - m) * kLog2e);
-      const size_t off = o_base + (size_t)i * o_stride + col;
-      f32x4 v;
+      const size_t off = o_base + (size_t)(i0 + i) * o_stride + col;
       if (kBf16Part && p.mode != kCombineShards) {
-        const bf16x4 hv = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.src_o) + off);
+        const bf16x8 hv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.src_o) + off);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (float)hv[e];
+        for (int e = 0; e < 4; ++e) {
+          acc0[e] += w * (float)hv[e];
+          acc1[e] += w * (float)hv[4 + e];
+        }
       } else {
-        v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.src_o) + off);
+        const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.src_o) + off);
+        acc0 += w * src[0];
+        acc1 += w * src[1];
       }
-      acc += w * v;
     }
   }
-  part[sg][tid & 31] = acc;
+  part[sg][2 * (tid & 15)] = acc0;
+  part[sg][2 * (tid & 15) + 1] = acc1;
   __syncthreads();
 
-  if (tid < 32) {
+  const float qnan = __builtin_nanf("");
+  const size_t orow = (size_t)b * p.rows + row;
+  if (tid < kCombineCols / 4) {
     f32x4 t = part[0][tid];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) t += part[j][tid];
+    for (int j = 1; j < kCombineGroups; ++j) t += part[j][tid];
     const float inv = 1.f / wsum;
     f32x4 o;
-    const float qnan = __builtin_nanf("");
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = bad ? qnan : (empty ? 0.f : t[e] * inv);
-    const size_t orow = (size_t)b * p.rows + row;
+    const int c0 = quarter * kCombineCols + 4 * tid;
     if (p.mode == kMergeShard) {
-      float* out = reinterpret_cast<float*>(p.out) + ((size_t)s_out * p.B * p.rows + orow) * kVDim + col;
+      float* out = reinterpret_cast<float*>(p.out) + ((size_t)s_out * p.B * p.rows + orow) * kVDim + c0;
       *reinterpret_cast<f32x4*>(out) = o;
     } else {
-      __bf16* out = reinterpret_cast<__bf16*>(p.out) + orow * kVDim + col;
+      __bf16* out = reinterpret_cast<__bf16*>(p.out) + orow * kVDim + c0;
       bf16x4 ob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
@@ -585,9 +764,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   }
   if (quarter != 0) return;
 
-  const float qnan = __builtin_nanf("");
   const float lse_all = bad ? qnan : (empty ? -INFINITY : m + __builtin_amdgcn_logf(wsum) * kLn2);
-  const size_t orow = (size_t)b * p.rows + row;
   if (p.mode == kMergeShard) {
     if (tid == 0) p.lse_shard[(size_t)s_out * p.B * p.rows + orow] = lse_all;
     return;
@@ -597,22 +774,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   // per-shard LSE over each shard's items: one wavefront per shard
   const int wave = tid >> 6, lane = tid & 63;
   for (int s = wave; s < p.shard_count; s += kThreads / 64) {
-    const int a0 = p.plan[b * p.shard_count + s];
-    const int a1 = p.plan[b * p.shard_count + s + 1];
+    const int a0 = p.plan[b * p.shard_count + s] - i0;
+    const int a1 = p.plan[b * p.shard_count + s + 1] - i0;
     float ms = -INFINITY;
-    for (int i = a0 + lane; i < a1; i += 64) ms = nan_max(ms, p.src_lse[(size_t)i * p.rows + row]);
+    for (int i = a0 + lane; i < a1; i += 64) ms = nan_max(ms, lse_of(i));
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) ms = nan_max(ms, __shfl_xor(ms, d, 64));
     float ws = 0.f;
     if (ms == ms && ms != -INFINITY)
       for (int i = a0 + lane; i < a1; i += 64) {
-        const float x = p.src_lse[(size_t)i * p.rows + row];
+        const float x = lse_of(i);
         if (x != -INFINITY) ws += __builtin_amdgcn_exp2f((x - ms) * kLog2e);
       }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) ws += __shfl_xor(ws, d, 64);
     if (lane == 0) {
-      float v = (ms != ms || bad) ? qnan : (ms == -INFINITY ? -INFINITY : ms + __builtin_amdgcn_logf(ws) * kLn2);
+      const float v = (ms != ms || bad) ? qnan : (ms == -INFINITY ? -INFINITY : ms + __builtin_amdgcn_logf(ws) * kLn2);
       p.lse_shard[(size_t)s * p.B * p.rows + orow] = v;
     }
   }

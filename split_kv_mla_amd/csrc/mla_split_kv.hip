@@ -17,25 +17,15 @@ namespace {
 
 using mla::ceil_div;
 
-// Workgroups the partial kernel aims to keep busy: one per compute unit of
-// an MI355X (256 CUs), each holding one 4-wave workgroup.
-int target_workgroups() {
-  static int cached = 0;
-  if (cached == 0) {
-    int v = 256;
-    if (const char* e = std::getenv("MLA_SPLIT_KV_TARGET_WGS")) {
-      const int x = std::atoi(e);
-      if (x > 0 && x <= (1 << 20)) v = x;
-    }
-    cached = v;
-  }
-  return cached;
-}
+// Workgroups the partial kernel keeps busy: one per compute unit of an MI355X
+// (256 CUs), each holding one 4-wave workgroup (the LDS ring and the
+// accumulators allow no second one).
+constexpr int kTargetWorkgroups = mla::kNumCUs;
 
-bool partials_in_bf16() {
-  const char* e = std::getenv("MLA_SPLIT_KV_PARTIAL_BF16");
-  return e && e[0] == '1';
-}
+// Item partials stay float32: a bf16 partial output would carry 2^-9 of its
+// own magnitude into the merged output, which is too much where partials of
+// large magnitude cancel (short rows, outlier values).
+constexpr bool kPartialsBf16 = false;
 
 int ilog2_exact(int v) {
   if (v <= 0 || (v & (v - 1))) return -1;
@@ -63,7 +53,7 @@ int check_args(const mla_decode_args* a) {
 }
 
 struct Plan {
-  int32_t pairs, row_groups, items_cap, tpi_min, tpi_max;
+  int32_t pairs, row_groups, items_cap, tpi_min, tpi_max, slots_per_wave;
   size_t plan_bytes, lse_bytes, o_bytes;
   size_t total() const { return plan_bytes + lse_bytes + o_bytes; }
 };
@@ -84,10 +74,13 @@ Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_coun
   for (int32_t s = shard_begin; s < shard_begin + shard_count; ++s)
     cap_tiles += ceil_div(mla::local_len(cap_tokens, a->num_shards, a->interleave, s), mla::kTile);
   cap_tiles *= a->batch;
+  // The device plan produces at most pairs + 4 waves of items, or, when the
+  // table window caps the item length, ceil(tiles / tpi_max) + pairs items.
+  p.slots_per_wave = std::max(1, kTargetWorkgroups / p.row_groups);
   const int64_t need = (cap_tiles + p.tpi_max - 1) / p.tpi_max + p.pairs;
-  const int64_t target = std::max<int64_t>(1, target_workgroups() / p.row_groups) + p.pairs;
-  p.items_cap = (int32_t)std::max<int64_t>(need, target);
-  const size_t part_elem = partials_in_bf16() ? 2 : 4;
+  const int64_t waves = (int64_t)p.pairs + 4 * (int64_t)p.slots_per_wave;
+  p.items_cap = (int32_t)std::max<int64_t>(need, waves);
+  const size_t part_elem = kPartialsBf16 ? 2 : 4;
   p.plan_bytes = round_up(sizeof(int32_t) * (size_t)(p.pairs + 2), 256);
   p.lse_bytes = round_up(sizeof(float) * (size_t)p.items_cap * rows_total, 256);
   p.o_bytes = round_up(part_elem * (size_t)p.items_cap * rows_total * mla::kVDim, 256);
@@ -116,19 +109,22 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   p.cap_tokens = a->max_blocks_per_seq * a->block_size;
   p.S = a->num_shards;
   p.I = a->interleave;
+  p.i_log2 = ilog2_exact(a->interleave);
   p.shard_begin = shard_begin;
   p.shard_count = shard_count;
   p.pairs = pl.pairs;
   p.items_cap = pl.items_cap;
   p.tpi_min = pl.tpi_min;
   p.tpi_max = pl.tpi_max;
+  p.slots_per_wave = pl.slots_per_wave;
   p.c_log2 = a->softmax_scale * mla::kLog2e;
   p.causal = a->causal ? 1 : 0;
   return p;
 }
 
 int launch_partial(const mla::DecodeParams& p, hipStream_t stream, bool bf16) {
-  const int grid = p.row_groups == 1 ? p.items_cap : ceil_div(p.items_cap, 8) * 8 * p.row_groups;
+  // persistent: one workgroup per compute unit walks all (item, row group) units
+  const int grid = mla::kNumCUs;
   if (bf16)
     hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(grid), dim3(mla::kThreads), 0, stream, p);
   else
@@ -173,7 +169,7 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   if (!out_partial || !lse || !workspace) return MLA_ERR_INVALID_ARG;
   const Plan pl = make_plan(a, shard_begin, shard_count);
   if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = partials_in_bf16();
+  const bool bf16 = kPartialsBf16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, shard_begin, shard_count, workspace);
   if ((st = launch_partial(p, s, bf16)) != MLA_OK) return st;
@@ -224,7 +220,7 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   if (!out || !lse || !workspace) return MLA_ERR_INVALID_ARG;
   const Plan pl = make_plan(a, 0, a->num_shards);
   if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = partials_in_bf16();
+  const bool bf16 = kPartialsBf16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, 0, a->num_shards, workspace);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return MLA_ERR_HIP;
