@@ -12,10 +12,18 @@ total exceeds the 256 MB Infinity Cache, so KV bytes come from HBM.  The
 partial kernel's own duration is measured live with HIP events recorded by the
 library on its stream (eager steps), and gives the roofline fraction.
 
+roofline.traffic comes from a committed counter summary
+(profiles/<kernel>_<workload>_counters.json, written by --summarize-counters
+from two rocprofv3 --pmc runs) and is reported only while the kernel sources
+still hash to what was profiled; otherwise it is null.
+
 Prints one JSON line.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -31,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "KV tokens/s + HBM GB/s (% of peak) for split-KV MLA decode + LSE combine"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 576 * 2
 
 
@@ -48,7 +57,85 @@ def parse():
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--min-kv-set-mb", type=float, default=640.0,
                     help="cycle KV copies until the cycled set exceeds this many MB")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run "
+                         "(both made with --calibrate-copy-mb) into the JSON summary bench.py reads")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("split_kv_mla_amd/csrc/mla_kernels.h", "split_kv_mla_amd/csrc/mla_plan.h",
+                  "split_kv_mla_amd/csrc/mla_split_kv.hip")
+PARTIAL_KERNEL = "mla::partial_kernel"
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"partial_kernel_{workload_name}_counters.json")
+
+
+def summarize_counters(fetch_dir, write_dir, workload_name, calib_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled to bytes by
+    what the same counter reads for the plain copy kernels of known size."""
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = {}
+        for row in csv.DictReader(open(files[0])):
+            if row["Counter_Name"] == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    known = calib_mib * 1024.0  # KiB read and written by each calibration copy
+    def factor(table, name_part):
+        hits = [v for k, v in table.items() if name_part in k]
+        return known / hits[0] if hits and hits[0] > 0 else None
+    rec = {
+        "workload": workload_name, "source_sha": kernel_source_sha(),
+        "calibration_mib": calib_mib,
+        "fetch_factor_blit_copy": factor(fetch, "copyBuffer"),
+        "write_factor_blit_copy": factor(write, "copyBuffer"),
+        "fetch_factor_elementwise_copy": factor(fetch, "neg_kernel") or factor(fetch, "NegFunctor")
+                                          or factor(fetch, "neg"),
+        "write_factor_elementwise_copy": factor(write, "neg_kernel") or factor(write, "NegFunctor")
+                                          or factor(write, "neg"),
+        "kernels": {},
+    }
+    ff, wf = rec["fetch_factor_blit_copy"], rec["write_factor_blit_copy"]
+    for k in sorted(set(fetch) | set(write)):
+        if "mla::" not in k:
+            continue
+        short = k.split("(")[0].replace("void ", "")
+        r_kib, w_kib = fetch.get(k), write.get(k)
+        rec["kernels"][short] = {
+            "fetch_kib_raw": r_kib, "write_kib_raw": w_kib,
+            "read_bytes": r_kib * ff * 1024 if (r_kib is not None and ff) else None,
+            "write_bytes": w_kib * wf * 1024 if (w_kib is not None and wf) else None,
+        }
+    return rec
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary, or None when there is none or the kernel changed since."""
+    path = counters_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(PARTIAL_KERNEL + "<false>")
+    if not k or k.get("read_bytes") is None or k.get("write_bytes") is None:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
 
 
 def algorithmic_bytes(w):
@@ -80,8 +167,19 @@ def cpu_baseline(w, budget_s):
                       f"on this workload, {el:.1f} s, numpy BLAS threads = {threads}"}
 
 
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        import workloads
+        name = workloads.STANDARD[args.workload]().name
+        calib = args.calibrate_copy_mb if args.calibrate_copy_mb > 0 else 256.0
+        print(json.dumps(summarize_counters(*args.summarize_counters, name, calib), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the shards are virtual, on one device)", file=sys.stderr)
@@ -94,10 +192,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy_mb > 0:
+        # counter calibration: a blit copy and an elementwise (negating) copy,
+        # each reading and writing exactly calibrate_copy_mb MiB
         n = int(args.calibrate_copy_mb * (1 << 20)) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     w = workloads.STANDARD[args.workload]()
@@ -136,6 +239,20 @@ def main():
     for e in evs:
         part_ms.append(e[0].elapsed_time(e[1]))
         comb_ms.append(e[1].elapsed_time(e[2]))
+
+    # one DCP rank's share: the partial kernel over shard 0 alone
+    rank_ms = []
+    sh_o = torch.empty((1, w.B, w.R, w.H, 512), dtype=torch.float32, device=dev)
+    sh_l = torch.empty((1, w.B, w.R, w.H), dtype=torch.float32, device=dev)
+    for i in range(args.event_steps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mla.mla_shard_decode_partial(q, kvs[i % copies], bt, sl, S, I, w.scale, w.causal, shard_begin=0,
+                                     shard_count=1, out_partial=sh_o, lse=sh_l, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            rank_ms.append(e0.elapsed_time(e1))
 
     # K steps in one graph, replayed between synchronisations
     K = args.steps
@@ -183,12 +300,16 @@ def main():
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "partial_kernel_ms": part_avg,
+        "partial_kernel_ms_p10_p50_p90": [pct(part_ms, 0.1), pct(part_ms, 0.5), pct(part_ms, 0.9)],
         "combine_kernel_ms": statistics.mean(comb_ms),
+        "combine_kernel_ms_p10_p50_p90": [pct(comb_ms, 0.1), pct(comb_ms, 0.5), pct(comb_ms, 0.9)],
+        "one_shard_partial_ms": statistics.median(rank_ms),
         "mfma_tflops_partial": flops / (part_avg / 1e3) / 1e12,
+        "mfma_frac_of_bf16_peak": flops / (part_avg / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "kv_copies_cycled": copies,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "mla::partial_kernel", "bytes_per_launch": kb},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(w.name),
+                     "kernel": PARTIAL_KERNEL, "bytes_per_launch": kb},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
