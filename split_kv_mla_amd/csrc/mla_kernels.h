@@ -302,33 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const Plan pl = make_plan(p, starts, scratch);
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
-
-  // Per-lane LDS offsets (independent of the item).
-  // DMA role: lane loads token tau of each tile, 16-byte pieces (lane & 7) ^ swz
-  // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
-  //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau))
-  const int dma_tau = wave * 8 + (lane >> 3);
-  const int dma_swz = ((lane & 7) ^ piece_swizzle(dma_tau)) * 16;
-  // K-read (A of S^T = K Q^T): lane reads token l32, piece 2*db + g.
-  const int kswz = piece_swizzle(l32);
-  const int kbase = (576 * (l32 >> 3) + 8 * (l32 & 7)) * 16;
-  int koff[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) koff[d] = kbase + (((2 * d + g) ^ kswz) * 16);
-  // V-read (A of O^T = V^T P^T) with the transposing read: 16-lane group
-  // (g, h) covers columns 32*db + 16*h .. +15 of tokens {4g+r} and {8+4g+r}.
-  const int h16 = (lane >> 4) & 1;
-  const int rr = (lane & 15) >> 2;
-  const int cc = lane & 3;
-  const int f1 = piece_swizzle(4 * g + rr);      // tokens 16*kb + 4g + rr
-  const int f2 = piece_swizzle(8 + 4 * g + rr);  // tokens 16*kb + 8 + 4g + rr
-  int voff1[2], voff2[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int pc = 4 * e + 2 * h16 + (cc >> 1);
-    voff1[e] = 128 * (4 * g + rr) + 16 * (pc ^ f1) + 8 * (cc & 1);
-    voff2[e] = 9216 + 128 * (4 * g + rr) + 16 * (pc ^ f2) + 8 * (cc & 1);
-  }
+  // this wavefront's slice of every ring stage (wave-uniform: a scalar register)
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_ring + (uint32_t)(wave * 9 * 1024));
 
   // Work units = (item, row group), walked by the persistent grid.  The row
   // groups of one item get unit ids congruent mod 8, and unit u runs on
@@ -345,6 +320,16 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       item = (k8 / G) * 8 + x;
     }
     if (item >= pl.n_items) continue;
+    // Per-lane LDS offsets (independent of the item), recomputed per unit from
+    // an opaque copy of the lane id: cheaper than keeping them live across units.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    // DMA role: lane loads token tau of each tile, 16-byte pieces (lane_o & 7) ^ swz
+    // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
+    //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau))
+    const int dma_tau = wave * 8 + (lane_o >> 3);
+    const int dma_swz = ((lane_o & 7) ^ piece_swizzle(dma_tau)) * 16;
+
     const int2 pk = find_pair(p, pl, item, starts, scratch);
     const int pair = pk.x;
     const int b = pair / p.shard_count;
@@ -377,33 +362,45 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
     const int lim_min = wave_min(lim);
 
-    // Tile kk of the pair into ring stage `stage`; tiles at or past nt re-read
-    // the item's last tile (the prologue's spare stages).
-    auto issue_tile = [&](int kk, int stage) {
+    // DMA source of this lane's 16-byte pieces of tile kk: tiles at or past nt
+    // re-read the item's last tile (the prologue's spare stages), and rows past
+    // the end re-read the last valid row (masked later).
+    auto tile_src = [&](int kk) -> const char* {
       kk = min(kk, tile1 - 1);
       int j = kk * kTile + dma_tau;
-      j = j < n_bs ? j : n_bs - 1;  // rows past the end re-read the last valid row (masked later)
+      j = j < n_bs ? j : n_bs - 1;
       // global position of local token j (shifts when I is a power of two)
       const int t = p.i_log2 >= 0 ? (((j >> p.i_log2) * S + s) << p.i_log2) | (j & (I - 1))
                                   : global_pos(j, S, I, s);
       const int phys = tbl[(t >> p.bs_log2) - blk_lo];
       const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
-      const char* src = reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds_ring + (uint32_t)(stage * kTileBytes + wave * 9 * 1024));
+      return reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
+    };
+    // 9 loads per wavefront: its 8 tokens x 1152 bytes of the tile into `stage`.
+    auto issue_src = [&](const char* src, int stage) {
+      const uint32_t dst = wave_lds + (uint32_t)(stage * kTileBytes);
 #pragma unroll
       for (int i = 0; i < 9; ++i) dma16(src + 128 * i, dst + 1024 * i);
     };
+    auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
-    // Prologue: tile 0, then Q (lane holds row l32, columns 16*db + 8*g .. +7)
-    // under the first tile's latency, then tiles 1 and 2.  Rows past
-    // rows_total load row 0 and never write.
+    // Prologue: tile 0, then Q (lane holds row l32, columns 16*db + 8*g ..
+    // +7) under the first tile's latency; both must be resident before the
+    // first tile anyway, and waiting for them here (the compiler waits before
+    // the register pin) keeps any wait for Q out of the tile loop.  Then tiles
+    // 1 and 2.  Rows past rows_total load row 0 and never write.
     issue_tile(tile0, 0);
     bf16x8 qf[36];
     {
-      const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + (row_ok ? row : 0)) * kHeadDim + 8 * g;
+      // wave-uniform base (scalar registers) + a per-lane offset
+      const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave);
+      const uint16_t* qwave = p.q + ((size_t)b * p.rows_total + row0) * kHeadDim;
+      int lane_q = lane;  // opaque copy: recomputing beats spilling the lane terms
+      asm volatile("" : "+v"(lane_q));
+      const int r_in = lane_q & 31;
+      const int qlane = (row0 + r_in < p.rows_total ? r_in : -row0) * kHeadDim + 8 * (lane_q >> 5);
 #pragma unroll
-      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qrow + 16 * db);
+      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qwave + qlane + 16 * db);
     }
 #pragma unroll
     for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
@@ -414,122 +411,152 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
     float l_run = 0.f;
 
-    // One pipelined walk over the item's tiles.  kMaxOnly: only the exact row
-    // maximum of the scores (written to m_ref).  Otherwise the softmax
-    // numerator and denominator against m_ref; m_ref is taken from the first
-    // tile that holds a token of the row, and if the denominator ends above
-    // 2^96 (some score exceeded the reference enough to endanger the fp32
-    // sums) the walk sets `overflow` instead of rescaling the accumulators.
+    // One pipelined walk over the item's tiles: iteration k multiplies tile k's
+    // V by P(k) while tile k+1's scores are formed, and turns those scores into
+    // P(k+1) under the last PV products, so the matrix pipe never waits for
+    // the softmax.  kMaxOnly: only the exact row maximum of the scores
+    // (written to m_ref).  Otherwise the softmax numerator and denominator
+    // against m_ref; m_ref is taken from the first tile that holds a token of
+    // the row, and if the denominator ends above 2^96 (some score exceeded the
+    // reference enough to endanger the fp32 sums) the walk sets `overflow`
+    // instead of rescaling the accumulators.
     constexpr float kSlackValue = 7.9228162514264337593543950336e28f;  // 2^96
+    struct PFrag {
+      bf16x8 hi[2], lo[2];
+    };
     auto walk = [&](auto max_only_tag, bool prologue_issued, bool& overflow) {
       constexpr bool kMaxOnly = decltype(max_only_tag)::value;
+      // LDS read offsets of this lane (from an opaque lane copy: recomputing
+      // them per walk beats keeping them live through the prologue)
+      int lane_r = lane;
+      asm volatile("" : "+v"(lane_r));
+      // K-read (A of S^T = K Q^T): lane reads token l32, piece 2*db + g.
+      const int kswz = piece_swizzle(lane_r & 31);
+      const int kbase = (576 * ((lane_r & 31) >> 3) + 8 * (lane_r & 7)) * 16;
+      int koff[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) koff[d] = kbase + (((2 * d + (lane_r >> 5)) ^ kswz) * 16);
+      // V-read (A of O^T = V^T P^T) with the transposing read: 16-lane group
+      // (g, h) covers columns 32*db + 16*h .. +15 of tokens {4g+r} and {8+4g+r}.
+      const int h16 = (lane_r >> 4) & 1;
+      const int rr = (lane_r & 15) >> 2;
+      const int cc = lane_r & 3;
+      const int f1 = piece_swizzle(4 * (lane_r >> 5) + rr);      // tokens 16*kb + 4g + rr
+      const int f2 = piece_swizzle(8 + 4 * (lane_r >> 5) + rr);  // tokens 16*kb + 8 + 4g + rr
+      int voff1[2], voff2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int pc = 4 * e + 2 * h16 + (cc >> 1);
+        voff1[e] = 128 * (4 * (lane_r >> 5) + rr) + 16 * (pc ^ f1) + 8 * (cc & 1);
+        voff2[e] = 9216 + 128 * (4 * (lane_r >> 5) + rr) + 16 * (pc ^ f2) + 8 * (cc & 1);
+      }
+      // K fragment db (A of S^T = K Q^T): token l32, columns 16*db + 8*g .. +7.
+      auto k_frag = [&](const char* buf, int db) {
+        return lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+      };
+      // V fragment f = 16*kb + db (A of O^T = V^T P^T): columns 32*db + l32 of
+      // tokens 16*kb + (8*g .. +7) in the order the P^T fragment uses.
+      auto v_frag = [&](const char* buf, int f) {
+        const int kb = f >> 4, db = f & 15;
+        const int off = 18432 * kb + 1024 * (db >> 1);
+        const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
+        const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+
       if (!prologue_issued)
         for (int k = 0; k < kStages - 1; ++k) issue_tile(tile0 + k, k);
+      const char* next_src = tile_src(tile0 + kStages - 1);
       float m_walk = -INFINITY;
-      for (int k = 0; k < nt; ++k) {
-        // tile k resident: the prologue always fills kStages-1 stages, so the
-        // younger loads in flight are min(2, nt-1-k), or the spare re-reads
-        // when the item has fewer than kStages-1 tiles
-        const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
-        if (younger >= 2) wait_vmcnt<18>();
-        else if (younger == 1) wait_vmcnt<9>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        const char* buf = ring + (k % kStages) * kTileBytes;
 
-        // S^T[token][row] for 32 tokens x 32 rows; LDS reads run kQkAhead MFMAs ahead.
-        f32x16 sc = f32x16{};
-        {
-          bf16x8 kf[36];
+      // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4))
+      // -> P^T fragments, or the running maximum.
+      auto soft = [&](f32x16 sc, int kt) -> PFrag {
+        // branch-free, so that it schedules into the matrix products around it
+        PFrag pf;
+        const int jt = (tile0 + kt) * kTile + 4 * g;
 #pragma unroll
-          for (int db = 0; db < 36; ++db) kf[db] = lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+        for (int i = 0; i < 16; ++i) sc[i] = (jt + 8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : sc[i];
+        float mx = sc[0];
 #pragma unroll
-          for (int db = 0; db < 36; ++db) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[db], qf[db], sc, 0, 0, 0);
-          constexpr int kQkAhead = 6;
-          __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
-#pragma unroll
-          for (int i = 0; i < 36 - kQkAhead; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
-        }
-        // Refill the stage freed by the previous tile while the score block drains
-        // out of the matrix pipe.
-        if (k + kStages - 1 < nt) issue_tile(tile0 + k + kStages - 1, (k + kStages - 1) % kStages);
-        // lane holds row l32 and tokens 8*(i/4) + 4*g + (i%4)
-        const int jt = (tile0 + k) * kTile;
-        if (jt + kTile > lim_min) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = jt + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (j >= lim) sc[i] = -INFINITY;
-          }
-        }
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
         if constexpr (kMaxOnly) {
-          float mx = sc[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-          m_walk = fmaxf(m_walk, fmaxf(mx, __shfl_xor(mx, 32, 64)) * c);
+          m_walk = fmaxf(m_walk, mx);
         } else {
           // The first tile that holds a token of the row fixes the reference
           // (nothing has been accumulated yet, so nothing is rescaled).
-          if (__any(m_ref == -INFINITY)) {
-            float mx = sc[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-            if (m_ref == -INFINITY) m_ref = mx;
-          }
+          m_ref = (m_ref == -INFINITY) ? mx : m_ref;
           const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
           // P = P_hi + P_lo, both bf16: a single bf16 P would cost up to 2^-8 of
           // relative weight per token, too much for rows of a few tokens or with
           // outlier values; the pair leaves a residual of at most 2^-16 p.
-          // The second half of the tile's P is formed under the first half's MFMAs.
-          bf16x8 pb[2], pl[2];
-          auto make_p = [&](int kb) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
               l_run += x;
               const __bf16 hi = (__bf16)x;
-              pb[kb][j] = hi;
-              pl[kb][j] = (__bf16)(x - (float)hi);
+              pf.hi[kb][j] = hi;
+              pf.lo[kb][j] = (__bf16)(x - (float)hi);
             }
-          };
-          make_p(0);
+        }
+        return pf;
+      };
+      // S^T of the tile in `buf` on its own (the first tile of the walk).
+      auto qk_alone = [&](const char* buf) {
+        f32x16 sc = f32x16{};
+        bf16x8 kf[36];
+#pragma unroll
+        for (int db = 0; db < 36; ++db) kf[db] = k_frag(buf, db);
+#pragma unroll
+        for (int db = 0; db < 36; ++db) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[db], qf[db], sc, 0, 0, 0);
+        constexpr int kAhead = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 36 - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        return sc;
+      };
+      // PV product i of a tile (64 per tile): fragment i/2, P_hi for even i, P_lo for odd.
+      auto pv_mfma = [&](const bf16x8* vf, const PFrag& pf, int i) {
+        const int f = i >> 1, kb = f >> 4, db = f & 15;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);
+      };
 
-          // O^T[dim][row] += V^T[dim][token] P^T[token][row]; the two transposing
-          // reads of a V fragment run kPvAhead fragments ahead of their MFMAs.
-          {
-            bf16x8 vf[32];
+      for (int k = 0; k < nt; ++k) {
+        // tile k resident: the prologue always fills kStages-1 stages, so the
+        // younger loads in flight are min(2, nt-1-k), or the spare re-reads
+        // when the item has fewer than kStages-1 tiles (Q, loaded between
+        // tiles 0 and 1, is resident with tile 0)
+        const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
+        if (younger >= 2) wait_vmcnt<18>();
+        else if (younger == 1) wait_vmcnt<9>();
+        else wait_vmcnt<0>();
+        // every wavefront is past tile k-1: its stage takes tile k+3
+        lds_barrier();
+        if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
+        next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
+        const char* buf = ring + (k % kStages) * kTileBytes;
+        const PFrag pf = soft(qk_alone(buf), k);
+        if constexpr (!kMaxOnly) {
+          bf16x8 vf[32];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+          for (int f = 0; f < 32; ++f) vf[f] = v_frag(buf, f);
 #pragma unroll
-              for (int db = 0; db < 16; ++db) {
-                const int off = 18432 * kb + 1024 * (db >> 1);
-                const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
-                const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
-                vf[16 * kb + db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-              }
+          for (int i = 0; i < 64; ++i) pv_mfma(vf, pf, i);
+          constexpr int kAhead = 6;
+          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              if (kb == 1) make_p(1);
-#pragma unroll
-              for (int db = 0; db < 16; ++db) {
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[16 * kb + db], pb[kb], acc[db], 0, 0, 0);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[16 * kb + db], pl[kb], acc[db], 0, 0, 0);
-              }
-            }
-            constexpr int kPvAhead = 3;
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 0);
-#pragma unroll
-            for (int i = 0; i < 32 - kPvAhead; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPvAhead, 0);
+          for (int i = 0; i < 32 - kAhead / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
+          __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
         }
       }
       if constexpr (kMaxOnly) {
@@ -539,7 +566,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         // inf/NaN): then the walk is redone from the exact maximum
         overflow |= !(l_run < kSlackValue);
       }
-      if constexpr (kMaxOnly) m_ref = m_walk;
     };
 
     using MaxOnly = std::integral_constant<bool, true>;
