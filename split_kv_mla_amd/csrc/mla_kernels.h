@@ -471,9 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
 
       // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4))
       // -> P^T fragments, or the running maximum.
-      auto soft = [&](f32x16 sc, int kt) -> PFrag {
-        // branch-free, so that it schedules into the matrix products around it
-        PFrag pf;
+      // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4)):
+      // masks the tokens at or past the row's end and returns the softmax
+      // reference, or (kMaxOnly) folds the row maximum into m_walk.
+      // Branch-free, so that it schedules among the matrix products.
+      auto prep = [&](f32x16& sc, int kt) -> float {
         const int jt = (tile0 + kt) * kTile + 4 * g;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = (jt + 8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : sc[i];
@@ -483,26 +485,34 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
         if constexpr (kMaxOnly) {
           m_walk = fmaxf(m_walk, mx);
+          return 0.f;
         } else {
           // The first tile that holds a token of the row fixes the reference
           // (nothing has been accumulated yet, so nothing is rescaled).
           m_ref = (m_ref == -INFINITY) ? mx : m_ref;
-          const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
-          // P = P_hi + P_lo, both bf16: a single bf16 P would cost up to 2^-8 of
-          // relative weight per token, too much for rows of a few tokens or with
-          // outlier values; the pair leaves a residual of at most 2^-16 p.
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
-              l_run += x;
-              const __bf16 hi = (__bf16)x;
-              pf.hi[kb][j] = hi;
-              pf.lo[kb][j] = (__bf16)(x - (float)hi);
-            }
+          return (m_ref == -INFINITY) ? 0.f : m_ref;
         }
-        return pf;
+      };
+      // Half kb of the tile's P^T fragments (tokens 16*kb + ...).  P = P_hi +
+      // P_lo, both bf16: a single bf16 P would cost up to 2^-8 of relative
+      // weight per token, too much for rows of a few tokens or with outlier
+      // values; the pair leaves a residual of at most 2^-16 p.
+      auto make_p1 = [&](PFrag& pf, const f32x16& sc, float msafe, int j) {
+        const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 + j], c, -msafe));
+        l_run += x;
+        const __bf16 hi = (__bf16)x;
+        pf.hi[1][j] = hi;
+        pf.lo[1][j] = (__bf16)(x - (float)hi);
+      };
+      auto make_p = [&](PFrag& pf, const f32x16& sc, float msafe, int kb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
+          l_run += x;
+          const __bf16 hi = (__bf16)x;
+          pf.hi[kb][j] = hi;
+          pf.lo[kb][j] = (__bf16)(x - (float)hi);
+        }
       };
       // S^T of the tile in `buf` on its own (the first tile of the walk).
       auto qk_alone = [&](const char* buf) {
@@ -542,21 +552,40 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
         next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
         const char* buf = ring + (k % kStages) * kTileBytes;
-        const PFrag pf = soft(qk_alone(buf), k);
+        f32x16 sc = qk_alone(buf);
+        const float msafe = prep(sc, k);
         if constexpr (!kMaxOnly) {
+          // O^T[dim][row] += V^T[dim][token] P^T[token][row]; the second half of
+          // P is formed under the first half's products
+          PFrag pf;
+          make_p(pf, sc, msafe, 0);
           bf16x8 vf[32];
+          // first 12 products (6 fragments) with their reads 6 ahead ...
 #pragma unroll
-          for (int f = 0; f < 32; ++f) vf[f] = v_frag(buf, f);
+          for (int f = 0; f < 9; ++f) vf[f] = v_frag(buf, f);
 #pragma unroll
-          for (int i = 0; i < 64; ++i) pv_mfma(vf, pf, i);
-          constexpr int kAhead = 6;
-          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+          for (int i = 0; i < 12; ++i) pv_mfma(vf, pf, i);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-          for (int i = 0; i < 32 - kAhead / 2; ++i) {
+          for (int i = 0; i < 6; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          // ... then the second half of P while they run in the matrix pipe ...
+          make_p(pf, sc, msafe, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          // ... then the other 52 products
+#pragma unroll
+          for (int f = 9; f < 32; ++f) vf[f] = v_frag(buf, f);
+#pragma unroll
+          for (int i = 12; i < 64; ++i) pv_mfma(vf, pf, i);
+#pragma unroll
+          for (int i = 0; i < 23; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         }
       }
       if constexpr (kMaxOnly) {
