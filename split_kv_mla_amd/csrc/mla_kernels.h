@@ -1,8 +1,8 @@
 // mla_kernels.h -- HIP kernels for gfx950 (CDNA4): split-KV MLA decode partials
 // and the exp2 LSE-weighted combine.
 //
-// Partial kernel (one workgroup = 4 wavefronts = one work item x one group of
-// 128 query rows):
+// Partial kernel (persistent: one workgroup per compute unit, 4 wavefronts,
+// each unit of work = one work item x one group of 128 query rows):
 //   * every workgroup derives the same work plan from seq_lens on the device:
 //     each (request, shard) pair's local tokens are cut into 32-token tiles and
 //     the tiles into items of equal length;
@@ -15,8 +15,11 @@
 //     transposing ds_read_b64_tr_b16, Q lives in VGPRs, the 32x512 accumulator
 //     of a wavefront in (A)VGPRs.  V is the first 512 columns of the same
 //     tile: it is never loaded twice;
-//   * online softmax in fp32 on base-2 scores, with lazy rescaling (the
-//     running max moves only when a tile's max exceeds it by 2^8);
+//   * softmax in fp32 on base-2 scores against a fixed reference: each row's
+//     maximum over the item's first tile (every row with a token in the item
+//     has one there).  Nothing is ever rescaled; if a later score exceeds the
+//     reference by so much that the fp32 denominator passes 2^96, the item is
+//     walked again, first for the exact row maximum, then against it;
 //   * each item writes a normalised partial output and its natural-log LSE;
 //     an item that holds no token of a row writes LSE = -inf and no output.
 // Combine kernel: one workgroup per (request, row, 128-wide slice of the 512
@@ -605,8 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     walk(Full{}, true, overflow);
     wait_vmcnt<0>();  // spare prologue re-reads of short items
     if (__syncthreads_or(overflow)) {
-      // Rare slow path: scores grew by more than 2^64 after the reference was
-      // fixed.  Find each row's exact maximum, then redo the walk against it.
+      // Rare slow path: a score exceeded the reference by enough to push the
+      // denominator past 2^96.  Find each row's exact maximum, then redo the walk
+      // against it.
       bool unused = false;
       walk(MaxOnly{}, false, unused);
       wait_vmcnt<0>();
