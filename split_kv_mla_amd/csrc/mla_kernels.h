@@ -49,6 +49,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
 constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
@@ -58,14 +60,17 @@ constexpr int kPlanPairsLds = 1024;               // per-pair item starts kept i
 constexpr int kTilesPerWave = 128;                // per-CU tile walks that justify one more item wave
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+// Item partial rows whose largest |o| is at most this are stored as fp16.
+constexpr float kHalfPartialMax = 2.0f;
 
 struct DecodeParams {
   const uint16_t* q;         // bf16 [B, R, H, 576]
   const uint16_t* kv;        // bf16 [num_blocks, block_size, 576]
   const int32_t* table;      // [B, max_blocks]
   const int32_t* seq_lens;   // [B]
-  void* part_o;              // [items_cap, rows_total, 512] fp32 or bf16
+  void* part_o;              // [items_cap, rows_total] slots of 512 fp32 (or 512 fp16 in the first half)
   float* part_lse;           // [items_cap, rows_total]
+  uint8_t* part_fmt;         // [items_cap, rows_total]: 1 = the slot holds fp16
   int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, tiles per item
   int32_t B, R, H, rows_total, row_groups;
   int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
@@ -286,18 +291,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 // ------------------------------------------------------------ partial kernel
 
-template <bool kBf16Part>
 __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
   __shared__ int tbl[kTableCache];
   __shared__ int starts[kPlanPairsLds + 1];
   __shared__ int scratch[16];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int g = lane >> 5;      // which half of the wavefront
-  const int l32 = lane & 31;
   const int S = p.S, I = p.I;
   const int bs_mask = (1 << p.bs_log2) - 1;
   const float c = p.c_log2;
@@ -305,8 +304,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const Plan pl = make_plan(p, starts, scratch);
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
-  // this wavefront's slice of every ring stage (wave-uniform: a scalar register)
-  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_ring + (uint32_t)(wave * 9 * 1024));
 
   // Work units = (item, row group), walked by the persistent grid.  The row
   // groups of one item get unit ids congruent mod 8, and unit u runs on
@@ -323,10 +320,18 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       item = (k8 / G) * 8 + x;
     }
     if (item >= pl.n_items) continue;
-    // Per-lane LDS offsets (independent of the item), recomputed per unit from
-    // an opaque copy of the lane id: cheaper than keeping them live across units.
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
+    // Lane-dependent values are recomputed per unit from an opaque copy of the
+    // thread id, so that none is hoisted out of the unit loop and kept live
+    // (and spilled) across the walks: recomputing them is cheaper.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;  // which half of the wavefront
+    const int l32 = lane & 31;
+    // this wavefront's slice of every ring stage (wave-uniform: a scalar register)
+    const uint32_t wave_lds = lds_ring + (uint32_t)(wave * 9 * 1024);
+    const int lane_o = lane;
     // DMA role: lane loads token tau of each tile, 16-byte pieces (lane_o & 7) ^ swz
     // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
     //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau))
@@ -625,26 +630,25 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (!row_ok) continue;
     const size_t prow = (size_t)item * p.rows_total + row;
     float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (bad) lse = __builtin_nanf("");
-    if (g == 0) p.part_lse[prow] = lse;
-    if (!(l_tot > 0.f)) continue;
-    const float inv = 1.f / l_tot;
+    if (row_ok && g == 0) p.part_lse[prow] = lse;
+    const bool live = row_ok && l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    // The row's largest |o| picks its storage: fp16 when it is at most
+    // kHalfPartialMax (rounding then moves no element by more than 2^-10, half
+    // the output's absolute tolerance, whatever the merge weights), else fp32.
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
+    const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
+    if (live && g == 0) p.part_fmt[prow] = as_half ? 1 : 0;
     // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3]
-    if constexpr (kBf16Part) {
-      __bf16* po = reinterpret_cast<__bf16*>(p.part_o) + prow * kVDim + 4 * g;
-#pragma unroll
-      for (int db = 0; db < 16; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * q + e] * inv);
-          *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * q) = v;
-        }
-    } else {
+    if (live && !as_half) {
       float* po = reinterpret_cast<float*>(p.part_o) + prow * kVDim + 4 * g;
 #pragma unroll
       for (int db = 0; db < 16; ++db)
@@ -655,6 +659,32 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
           *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q) = v;
         }
+    }
+    // fp16 rows leave through the idle ring, transposed so that one store
+    // writes a whole 1 KiB row (the scattered 8-byte pieces of the register
+    // layout would cost a write request each).  Each wavefront uses its own
+    // region (32 rows of 1040 bytes), so only its own LDS order matters.
+    {
+      constexpr int kStride = 2 * kVDim + 16;  // bytes per staged row (16 of padding)
+      char* stage = ring + wave * (kRowsPerWave * kStride);
+#pragma unroll
+      for (int db = 0; db < 16; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[db][4 * q + e] * inv);
+          *reinterpret_cast<f16x4*>(stage + l32 * kStride + 2 * (32 * db + 8 * q + 4 * g)) = v;
+        }
+      asm volatile("" ::: "memory");  // the reads below see every lane's writes
+      const uint64_t half_rows = __ballot(as_half && g == 0);  // bit r: row l32 = r
+      const size_t prow0 = (size_t)item * p.rows_total + rg * kRowsPerGroup + wave * kRowsPerWave;
+      _Float16* po = reinterpret_cast<_Float16*>(p.part_o) + prow0 * (2 * kVDim) + 8 * lane;
+#pragma unroll 4
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride + 16 * lane);
+        if ((half_rows >> r) & 1) *reinterpret_cast<f32x4*>(po + (size_t)r * (2 * kVDim)) = v;
+      }
     }
   }
 }
@@ -670,6 +700,7 @@ enum CombineMode : int32_t {
 struct CombineParams {
   const void* src_o;        // items: [items_cap, rows, 512]; shards: [S, B, rows, 512] fp32
   const float* src_lse;     // items: [items_cap, rows]; shards: [S, B, rows]
+  const uint8_t* src_fmt;   // items: [items_cap, rows], 1 = fp16 slot; NULL = all fp32
   const int32_t* plan;      // [pairs + 2] from the partial kernel (item modes)
   const int32_t* seq_lens;  // [B] (item modes; NULL in kCombineShards)
   int32_t cap_tokens;
@@ -704,9 +735,9 @@ constexpr int kCombineCols = 128;             // output columns per workgroup
 constexpr int kCombineGroups = 16;            // source groups per workgroup
 constexpr int kCombineLdsSources = 2048;      // source LSEs staged in LDS
 
-template <bool kBf16Part>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float src_lse[kCombineLdsSources];
+  __shared__ uint8_t src_fmt[kCombineLdsSources];
   __shared__ f32x4 part[kCombineGroups][kCombineCols / 4];
   __shared__ float red[8];
 
@@ -751,12 +782,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   auto lse_of = [&](int i) -> float {  // i relative to i0
     return staged ? src_lse[i] : p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
   };
+  auto fmt_at = [&](int i) -> int {  // straight from memory; 0 = fp32 slot
+    return p.src_fmt ? p.src_fmt[l_base + (size_t)(i0 + i) * l_stride] : 0;
+  };
 
   // pass 1: stage the source LSEs, their max, and the total weight
   float m = -INFINITY;
   for (int i = tid; i < n; i += kThreads) {
     const float x = p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
-    if (staged) src_lse[i] = x;
+    if (staged) {
+      src_lse[i] = x;
+      src_fmt[i] = (uint8_t)fmt_at(i);
+    }
     m = nan_max(m, x);
   }
   m = block_reduce(m, true, red);  // its barriers also publish src_lse
@@ -780,9 +817,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       const float x = lse_of(i);
       if (x == -INFINITY) continue;  // empty source: its payload is never read
       const float w = __builtin_amdgcn_exp2f((x - m) * kLog2e);
-      const size_t off = o_base + (size_t)(i0 + i) * o_stride + col;
-      if (kBf16Part && p.mode != kCombineShards) {
-        const bf16x8 hv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.src_o) + off);
+      const size_t off = o_base + (size_t)(i0 + i) * o_stride + col;  // in floats
+      if (staged ? src_fmt[i] : fmt_at(i)) {
+        // an fp16 slot: the same columns in the first half of the slot
+        const f16x8 hv = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.src_o) + 2 * off - col);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc0[e] += w * (float)hv[e];

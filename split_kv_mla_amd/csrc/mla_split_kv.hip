@@ -22,10 +22,9 @@ using mla::ceil_div;
 // accumulators allow no second one).
 constexpr int kTargetWorkgroups = mla::kNumCUs;
 
-// Item partials stay float32: a bf16 partial output would carry 2^-9 of its
-// own magnitude into the merged output, which is too much where partials of
-// large magnitude cancel (short rows, outlier values).
-constexpr bool kPartialsBf16 = false;
+// Item partial slots are sized for float32; the partial kernel stores a row as
+// fp16 (in the slot's first half) when that is accurate enough (see
+// kHalfPartialMax) and records the choice per row.
 
 int ilog2_exact(int v) {
   if (v <= 0 || (v & (v - 1))) return -1;
@@ -54,8 +53,8 @@ int check_args(const mla_decode_args* a) {
 
 struct Plan {
   int32_t pairs, row_groups, items_cap, tpi_min, tpi_max, slots_per_wave;
-  size_t plan_bytes, lse_bytes, o_bytes;
-  size_t total() const { return plan_bytes + lse_bytes + o_bytes; }
+  size_t plan_bytes, lse_bytes, fmt_bytes, o_bytes;
+  size_t total() const { return plan_bytes + lse_bytes + fmt_bytes + o_bytes; }
 };
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -80,10 +79,10 @@ Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_coun
   const int64_t need = (cap_tiles + p.tpi_max - 1) / p.tpi_max + p.pairs;
   const int64_t waves = (int64_t)p.pairs + 4 * (int64_t)p.slots_per_wave;
   p.items_cap = (int32_t)std::max<int64_t>(need, waves);
-  const size_t part_elem = kPartialsBf16 ? 2 : 4;
   p.plan_bytes = round_up(sizeof(int32_t) * (size_t)(p.pairs + 2), 256);
   p.lse_bytes = round_up(sizeof(float) * (size_t)p.items_cap * rows_total, 256);
-  p.o_bytes = round_up(part_elem * (size_t)p.items_cap * rows_total * mla::kVDim, 256);
+  p.fmt_bytes = round_up((size_t)p.items_cap * rows_total, 256);
+  p.o_bytes = round_up(sizeof(float) * (size_t)p.items_cap * rows_total * mla::kVDim, 256);
   return p;
 }
 
@@ -97,7 +96,8 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   char* w = static_cast<char*>(ws);
   p.plan_out = reinterpret_cast<int32_t*>(w);
   p.part_lse = reinterpret_cast<float*>(w + pl.plan_bytes);
-  p.part_o = w + pl.plan_bytes + pl.lse_bytes;
+  p.part_fmt = reinterpret_cast<uint8_t*>(w + pl.plan_bytes + pl.lse_bytes);
+  p.part_o = w + pl.plan_bytes + pl.lse_bytes + pl.fmt_bytes;
   p.B = a->batch;
   p.R = a->rows;
   p.H = a->heads;
@@ -122,23 +122,15 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   return p;
 }
 
-int launch_partial(const mla::DecodeParams& p, hipStream_t stream, bool bf16) {
+int launch_partial(const mla::DecodeParams& p, hipStream_t stream) {
   // persistent: one workgroup per compute unit walks all (item, row group) units
-  const int grid = mla::kNumCUs;
-  if (bf16)
-    hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(grid), dim3(mla::kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mla::partial_kernel<false>, dim3(grid), dim3(mla::kThreads), 0, stream, p);
+  hipLaunchKernelGGL(mla::partial_kernel, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-int launch_combine(const mla::CombineParams& c, int64_t units, hipStream_t stream, bool bf16) {
+int launch_combine(const mla::CombineParams& c, int64_t units, hipStream_t stream) {
   if (units * 4 > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  const int grid = (int)(units * 4);
-  if (bf16)
-    hipLaunchKernelGGL(mla::combine_kernel<true>, dim3(grid), dim3(mla::kThreads), 0, stream, c);
-  else
-    hipLaunchKernelGGL(mla::combine_kernel<false>, dim3(grid), dim3(mla::kThreads), 0, stream, c);
+  hipLaunchKernelGGL(mla::combine_kernel, dim3((int)(units * 4)), dim3(mla::kThreads), 0, stream, c);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -169,13 +161,13 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   if (!out_partial || !lse || !workspace) return MLA_ERR_INVALID_ARG;
   const Plan pl = make_plan(a, shard_begin, shard_count);
   if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = kPartialsBf16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, shard_begin, shard_count, workspace);
-  if ((st = launch_partial(p, s, bf16)) != MLA_OK) return st;
+  if ((st = launch_partial(p, s)) != MLA_OK) return st;
   mla::CombineParams c{};
   c.src_o = p.part_o;
   c.src_lse = p.part_lse;
+  c.src_fmt = p.part_fmt;
   c.plan = p.plan_out;
   c.seq_lens = a->seq_lens;
   c.cap_tokens = p.cap_tokens;
@@ -187,7 +179,7 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   c.rows = p.rows_total;
   c.shard_count = shard_count;
   c.mode = mla::kMergeShard;
-  return launch_combine(c, (int64_t)shard_count * a->batch * p.rows_total, s, bf16);
+  return launch_combine(c, (int64_t)shard_count * a->batch * p.rows_total, s);
 }
 
 int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
@@ -199,6 +191,7 @@ int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shar
   mla::CombineParams c{};
   c.src_o = out_partial;
   c.src_lse = lse;
+  c.src_fmt = nullptr;  // caller partials are float32
   c.plan = nullptr;
   c.seq_lens = nullptr;
   c.items_cap = 0;
@@ -209,7 +202,7 @@ int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shar
   c.rows = rows * heads;
   c.shard_count = num_shards;
   c.mode = mla::kCombineShards;
-  return launch_combine(c, (int64_t)batch * c.rows, static_cast<hipStream_t>(stream), false);
+  return launch_combine(c, (int64_t)batch * c.rows, static_cast<hipStream_t>(stream));
 }
 
 int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* workspace,
@@ -220,15 +213,15 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   if (!out || !lse || !workspace) return MLA_ERR_INVALID_ARG;
   const Plan pl = make_plan(a, 0, a->num_shards);
   if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = kPartialsBf16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, 0, a->num_shards, workspace);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return MLA_ERR_HIP;
-  if ((st = launch_partial(p, s, bf16)) != MLA_OK) return st;
+  if ((st = launch_partial(p, s)) != MLA_OK) return st;
   if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), s) != hipSuccess) return MLA_ERR_HIP;
   mla::CombineParams c{};
   c.src_o = p.part_o;
   c.src_lse = p.part_lse;
+  c.src_fmt = p.part_fmt;
   c.plan = p.plan_out;
   c.seq_lens = a->seq_lens;
   c.cap_tokens = p.cap_tokens;
@@ -240,7 +233,7 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   c.rows = p.rows_total;
   c.shard_count = a->num_shards;
   c.mode = mla::kCombineItems;
-  if ((st = launch_combine(c, (int64_t)a->batch * p.rows_total, s, bf16)) != MLA_OK) return st;
+  if ((st = launch_combine(c, (int64_t)a->batch * p.rows_total, s)) != MLA_OK) return st;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
