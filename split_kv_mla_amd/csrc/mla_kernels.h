@@ -112,6 +112,20 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) 
   return off + incl - v;
 }
 
+// OR of a flag over the 256-thread workgroup, with a barrier: a wave vote,
+// one LDS word per wave (slots[0..3] of a caller-provided LDS array).  Cheaper
+// than the generic block vote, which reads the dispatch packet for the block
+// shape.
+// `wave` and `lane` are the caller's (wave-uniform / per-lane) indices.
+__device__ __forceinline__ bool block_any(bool v, int* slots, int wave, int lane) {
+  const bool wv = __any(v);
+  if (lane == 0) slots[wave] = wv ? 1 : 0;
+  __syncthreads();
+  const bool r = (slots[0] | slots[1] | slots[2] | slots[3]) != 0;
+  __syncthreads();  // the slots can be reused after this
+  return r;
+}
+
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
@@ -278,6 +292,21 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
+// 4 bytes per active lane from global memory straight into LDS: lane i writes
+// LDS bytes [lds_base + 4 i, +4).  Same conventions as dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gaddr), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -348,6 +377,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int tile1 = min(tile0 + pl.tpi, ceil_div(n_bs, kTile));
     const int nt = tile1 - tile0;
 
+    // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
+    const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
+    const bool row_ok = row < p.rows_total;
+    const int r = row_ok ? row / p.H : 0;
+    const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
+    const int lim_min = wave_min(lim);
+
     // The previous unit is done with the ring and the table window.
     __syncthreads();
 
@@ -355,20 +391,41 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
     const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
     const int span = blk_hi - blk_lo + 1;
+    // The window goes straight to LDS; Q (lane holds row l32, columns
+    // 16*db + 8*g .. +7; rows past rows_total load row 0 and never write) is
+    // loaded behind it, so the wait for the window leaves Q in flight.
+    {
+      const int32_t* trow = p.table + (size_t)b * p.max_blocks + blk_lo;
+      const uint32_t tbl_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)tbl;
+      for (int i0 = 0; i0 < span; i0 += kThreads) {
+        const int i = i0 + tid;
+        if (i < span) dma4(trow + i, __builtin_amdgcn_readfirstlane(tbl_lds + 4u * (uint32_t)(i0 + wave * 64)));
+      }
+    }
+    bf16x8 qf[36];
+    {
+      // wave-uniform base (scalar registers) + a per-lane offset
+      const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave);
+      const uint16_t* qwave = p.q + ((size_t)b * p.rows_total + row0) * kHeadDim;
+      int lane_q = lane;  // opaque copy: recomputing beats spilling the lane terms
+      asm volatile("" : "+v"(lane_q));
+      const int r_in = lane_q & 31;
+      const int qlane = (row0 + r_in < p.rows_total ? r_in : -row0) * kHeadDim + 8 * (lane_q >> 5);
+#pragma unroll
+      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qwave + qlane + 16 * db);
+    }
+    wait_vmcnt<36>();  // the window has landed (only the 36 Q loads are younger)
+    __syncthreads();
     bool bad = false;
     for (int i = tid; i < span; i += kThreads) {
-      int v = p.table[(size_t)b * p.max_blocks + blk_lo + i];
-      if ((unsigned)v >= (unsigned)p.num_blocks) { v = 0; bad = true; }
-      tbl[i] = v;
+      const int v = tbl[i];
+      if ((unsigned)v >= (unsigned)p.num_blocks) {  // never address outside the cache
+        tbl[i] = 0;
+        bad = true;
+      }
     }
-    bad = __syncthreads_or(bad);
+    bad = block_any(bad, scratch + 12, wave, lane);
 
-    // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
-    const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
-    const bool row_ok = row < p.rows_total;
-    const int r = row_ok ? row / p.H : 0;
-    const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
-    const int lim_min = wave_min(lim);
 
     // DMA source of this lane's 16-byte pieces of tile kk: tiles at or past nt
     // re-read the item's last tile (the prologue's spare stages), and rows past
@@ -392,24 +449,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     };
     auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
-    // Prologue: tile 0, then Q (lane holds row l32, columns 16*db + 8*g ..
-    // +7) under the first tile's latency; both must be resident before the
-    // first tile anyway, and waiting for them here (the compiler waits before
-    // the register pin) keeps any wait for Q out of the tile loop.  Then tiles
-    // 1 and 2.  Rows past rows_total load row 0 and never write.
+    // Prologue: tile 0; Q (loaded above, behind the table window) and tile 0
+    // must both be resident before the first tile, and waiting for them here
+    // (the compiler waits before the register pin) keeps any wait for Q out of
+    // the tile loop.  Then tiles 1 and 2.
     issue_tile(tile0, 0);
-    bf16x8 qf[36];
-    {
-      // wave-uniform base (scalar registers) + a per-lane offset
-      const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave);
-      const uint16_t* qwave = p.q + ((size_t)b * p.rows_total + row0) * kHeadDim;
-      int lane_q = lane;  // opaque copy: recomputing beats spilling the lane terms
-      asm volatile("" : "+v"(lane_q));
-      const int r_in = lane_q & 31;
-      const int qlane = (row0 + r_in < p.rows_total ? r_in : -row0) * kHeadDim + 8 * (lane_q >> 5);
-#pragma unroll
-      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qwave + qlane + 16 * db);
-    }
 #pragma unroll
     for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
     issue_tile(tile0 + 1, 1);
@@ -612,7 +656,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     bool overflow = false;
     walk(Full{}, true, overflow);
     wait_vmcnt<0>();  // spare prologue re-reads of short items
-    if (__syncthreads_or(overflow)) {
+    if (block_any(overflow, scratch + 12, wave, lane)) {
       // Rare slow path: a score exceeded the reference by enough to push the
       // denominator past 2^96.  Find each row's exact maximum, then redo the walk
       // against it.
