@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--workload", default="long",
                     choices=["long", "long_b2", "batch", "verify", "padded", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-one-shard", action="store_true",
+                    help="skip the one-shard partial launches (profiled runs, so that every "
+                         "partial-kernel dispatch is a full step's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -91,25 +94,30 @@ def summarize_counters(fetch_dir, write_dir, workload_name, calib_mib):
         for row in csv.DictReader(open(files[0])):
             if row["Counter_Name"] == counter:
                 vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-        return {k: statistics.mean(v) for k, v in vals.items()}
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
+        return vals
+    fetch_all = per_kernel(fetch_dir, "FETCH_SIZE")
+    write_all = per_kernel(write_dir, "WRITE_SIZE")
+    fetch = {k: statistics.mean(v) for k, v in fetch_all.items()}
+    write = {k: statistics.mean(v) for k, v in write_all.items()}
     known = calib_mib * 1024.0  # KiB read and written by each calibration copy
-    def factor(table, name_part):
-        hits = [v for k, v in table.items() if name_part in k]
+    def factor(table_all, name_part):
+        # the calibration copy is the largest dispatch of its kernel (the runtime
+        # also uses the blit kernel for the small host-to-device uploads)
+        hits = [max(v) for k, v in table_all.items() if name_part in k]
         return known / hits[0] if hits and hits[0] > 0 else None
     rec = {
         "workload": workload_name, "source_sha": kernel_source_sha(),
         "calibration_mib": calib_mib,
-        "fetch_factor_blit_copy": factor(fetch, "copyBuffer"),
-        "write_factor_blit_copy": factor(write, "copyBuffer"),
-        "fetch_factor_elementwise_copy": factor(fetch, "neg_kernel") or factor(fetch, "NegFunctor")
-                                          or factor(fetch, "neg"),
-        "write_factor_elementwise_copy": factor(write, "neg_kernel") or factor(write, "NegFunctor")
-                                          or factor(write, "neg"),
+        "fetch_factor_blit_copy": factor(fetch_all, "copyBuffer"),
+        "write_factor_blit_copy": factor(write_all, "copyBuffer"),
+        "fetch_factor_elementwise_copy": factor(fetch_all, "neg"),
+        "write_factor_elementwise_copy": factor(write_all, "neg"),
         "kernels": {},
     }
-    ff, wf = rec["fetch_factor_blit_copy"], rec["write_factor_blit_copy"]
+    # Scale by the elementwise copy: like the mla kernels it moves whole 128-byte
+    # lines with 16-byte lane accesses (the blit copy's factors are kept as a check).
+    ff, wf = rec["fetch_factor_elementwise_copy"], rec["write_factor_elementwise_copy"]
+    rec["scaled_by"] = "elementwise_copy"
     for k in sorted(set(fetch) | set(write)):
         if "mla::" not in k:
             continue
@@ -132,7 +140,7 @@ def load_traffic(workload_name):
     rec = json.load(open(path))
     if rec.get("source_sha") != kernel_source_sha():
         return None
-    k = rec.get("kernels", {}).get(PARTIAL_KERNEL + "<false>")
+    k = rec.get("kernels", {}).get(PARTIAL_KERNEL)
     if not k or k.get("read_bytes") is None or k.get("write_bytes") is None:
         return None
     return k["read_bytes"] + k["write_bytes"]
@@ -242,9 +250,10 @@ def main():
 
     # one DCP rank's share: the partial kernel over shard 0 alone
     rank_ms = []
+    n_one_shard = 0 if args.no_one_shard else args.event_steps + 2
     sh_o = torch.empty((1, w.B, w.R, w.H, 512), dtype=torch.float32, device=dev)
     sh_l = torch.empty((1, w.B, w.R, w.H), dtype=torch.float32, device=dev)
-    for i in range(args.event_steps + 2):
+    for i in range(n_one_shard):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         mla.mla_shard_decode_partial(q, kvs[i % copies], bt, sl, S, I, w.scale, w.causal, shard_begin=0,
@@ -303,7 +312,7 @@ def main():
         "partial_kernel_ms_p10_p50_p90": [pct(part_ms, 0.1), pct(part_ms, 0.5), pct(part_ms, 0.9)],
         "combine_kernel_ms": statistics.mean(comb_ms),
         "combine_kernel_ms_p10_p50_p90": [pct(comb_ms, 0.1), pct(comb_ms, 0.5), pct(comb_ms, 0.9)],
-        "one_shard_partial_ms": statistics.median(rank_ms),
+        "one_shard_partial_ms": statistics.median(rank_ms) if rank_ms else None,
         "mfma_tflops_partial": flops / (part_avg / 1e3) / 1e12,
         "mfma_frac_of_bf16_peak": flops / (part_avg / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "kv_copies_cycled": copies,
