@@ -56,8 +56,7 @@ constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
 constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
 constexpr int kRowsPerGroup = 4 * kRowsPerWave;   // 128 query rows per workgroup
 constexpr int kNumCUs = 256;                      // MI355X compute units: the persistent grid
-constexpr int kPlanPairsLds = 1024;               // per-pair item starts kept in LDS
-constexpr int kTilesPerWave = 128;                // per-CU tile walks that justify one more item wave
+constexpr int kPlanPairsLds = 960;                // per-pair plan prefixes kept in LDS
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 // Item partial rows whose largest |o| is at most this are stored as fp16.
@@ -76,8 +75,8 @@ struct DecodeParams {
   int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
   int32_t S, I, shard_begin, shard_count, pairs;
   int32_t i_log2;            // log2(I) when I is a power of two, else -1
-  int32_t items_cap, tpi_min, tpi_max;
-  int32_t slots_per_wave;    // work units one wave of workgroups holds per row group
+  int32_t items_cap, tpi_max;
+  int32_t slots;             // workgroup slots per row group: 8 * floor(32 / row_groups)
   float c_log2;              // softmax_scale * log2(e)
   int32_t causal;
 };
@@ -160,100 +159,112 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
 }
 
 struct Plan {
-  int tpi;      // tiles per item
+  int U;        // tiles per grid cell: no item crosses a cell boundary
+  int W;        // cost units per workgroup slot (a multiple of U)
+  int T;        // cost units of the launch
   int n_items;  // items of the launch (per row group)
 };
 
-// The split of every (request, shard) pair's tiles into items, identical in
-// every workgroup.  Items per row group aim at W waves of the grid (W from the
-// total work); pairs with tokens each take at least one item.  Item starts per
-// pair go to `starts` (LDS) when the pairs fit, and workgroup 0 publishes them
-// with the item total and tiles-per-item for the combine.
-__device__ Plan make_plan(const DecodeParams& p, int* starts, int* scratch) {
+// The split of the launch into items, identical in every workgroup.  Pairs
+// are laid end to end on a cost axis, each non-empty pair taking kPieceCost
+// units (the prologue and epilogue of one more item) followed by one unit per
+// tile; the axis is cut into equal ranges, one per workgroup slot, and the
+// ranges into cells of U tiles (U no larger than the table window allows).
+// An item is the part of one pair's tiles inside one cell, so every slot has
+// the same cost give or take one cell's rounding.  Cost and item prefixes per
+// pair go to `cstart` / `starts` (LDS) when the pairs fit, and workgroup 0
+// publishes the item prefixes with the item total and U for the combine.
+__device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* scratch) {
   const int P = p.pairs;
   const bool in_reg = P <= kThreads;
   const int my_t = (in_reg && (int)threadIdx.x < P) ? pair_tiles(p, threadIdx.x) : 0;
-  auto pair_sum = [&](auto f) -> int {
-    if (in_reg) return block_sum(f(my_t), scratch);
-    int tot = 0;
-    for (int base = 0; base < P; base += kThreads) {
-      const int pr = base + (int)threadIdx.x;
-      tot += block_sum(pr < P ? f(pair_tiles(p, pr)) : 0, scratch);
+  int T = 0;
+  if (in_reg) {
+    T = block_sum(pair_cost(my_t), scratch);
+  } else {
+    for (int b0 = 0; b0 < P; b0 += kThreads) {
+      const int pr = b0 + (int)threadIdx.x;
+      T += block_sum(pr < P ? pair_cost(pair_tiles(p, pr)) : 0, scratch);
     }
-    return tot;
-  };
-  const int T = pair_sum([](int t) { return t; });
-  const int nonempty = pair_sum([](int t) { return t > 0 ? 1 : 0; });
-  const int64_t walks = (int64_t)T * p.row_groups;
-  int W = (int)((walks + (int64_t)kNumCUs * kTilesPerWave - 1) / ((int64_t)kNumCUs * kTilesPerWave));
-  W = W < 1 ? 1 : (W > 4 ? 4 : W);
-  const int base = p.slots_per_wave * W;
-  const bool many_pairs = nonempty > base / 2;
-  const int target = min(many_pairs ? nonempty + base : base, p.items_cap);
-  const int free_slots = max(1, target - (many_pairs ? nonempty : 0));
-  int tpi = min(p.tpi_max, max(p.tpi_min, ceil_div(max(T, 1), free_slots)));
-  int n = 0;
-  for (int it = 0;; ++it) {
-    const int t_cur = tpi;
-    n = pair_sum([t_cur](int t) { return ceil_div(t, t_cur); });
-    if (n <= target || tpi >= p.tpi_max || it >= 6) break;
-    tpi = min(p.tpi_max, max(tpi + 1, (int)(((int64_t)tpi * n + target - 1) / target)));
   }
-  if (n > p.items_cap) {  // never exceed the slots the host sized for
-    tpi = p.tpi_max;
-    const int t_cur = tpi;
-    n = pair_sum([t_cur](int t) { return ceil_div(t, t_cur); });
-  }
+  const int wmin = max(1, ceil_div(T, p.slots));
+  const int m = ceil_div(wmin, p.tpi_max);
+  const int U = ceil_div(wmin, m);
+  const bool keep = P <= kPlanPairsLds;
   const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
-  if (P <= kPlanPairsLds || publish) {
-    int run = 0;
+  int crun = 0, irun = 0;
+  if (keep || publish) {
     for (int b0 = 0; b0 < P; b0 += kThreads) {
       const int pr = b0 + (int)threadIdx.x;
       const int t = in_reg ? my_t : (pr < P ? pair_tiles(p, pr) : 0);
-      const int cnt = pr < P ? ceil_div(t, tpi) : 0;
-      int tot;
-      const int ex = block_excl_scan(cnt, scratch, &tot);
+      int ctot, itot;
+      const int cex = crun + block_excl_scan(pr < P ? pair_cost(t) : 0, scratch, &ctot);
+      const int iex = irun + block_excl_scan(pr < P ? pair_items(cex + kPieceCost, t, U) : 0, scratch, &itot);
       if (pr < P) {
-        if (P <= kPlanPairsLds) starts[pr] = run + ex;
-        if (publish) p.plan_out[pr] = run + ex;
+        if (keep) {
+          cstart[pr] = cex;
+          starts[pr] = iex;
+        }
+        if (publish) p.plan_out[pr] = iex;
       }
-      run += tot;
+      crun += ctot;
+      irun += itot;
     }
     if (threadIdx.x == 0) {
-      if (P <= kPlanPairsLds) starts[P] = run;
-      if (publish) { p.plan_out[P] = run; p.plan_out[P + 1] = tpi; }
+      if (keep) {
+        cstart[P] = crun;
+        starts[P] = irun;
+      }
+      if (publish) {
+        p.plan_out[P] = irun;
+        p.plan_out[P + 1] = U;
+      }
     }
   }
   __syncthreads();
-  return Plan{tpi, n};
+  return Plan{U, m * U, T, irun};
 }
 
-// Pair holding `item` and the item's first item index within that pair.
-__device__ int2 find_pair(const DecodeParams& p, const Plan& pl, int item, const int* starts, int* scratch) {
+struct PairAt {
+  int pair;    // the pair whose cost range holds the position
+  int cstart;  // its first cost unit
+  int cend;    // one past its last
+  int istart;  // its first item
+};
+
+// The non-empty pair whose cost range holds cost position x (0 <= x < T).
+__device__ PairAt pair_at(const DecodeParams& p, const Plan& pl, int x, const int* starts, const int* cstart,
+                          int* scratch) {
   const int P = p.pairs;
   if (P <= kPlanPairsLds) {
-    int lo = 0, hi = P;  // largest pr with starts[pr] <= item
+    int lo = 0, hi = P;  // largest pr with cstart[pr] <= x: empty pairs share the next one's start
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (starts[mid] <= item) lo = mid; else hi = mid;
+      if (cstart[mid] <= x) lo = mid; else hi = mid;
     }
-    while (lo + 1 < P && starts[lo + 1] <= item) ++lo;  // skip pairs without items
-    return make_int2(lo, starts[lo]);
+    return PairAt{lo, cstart[lo], cstart[lo + 1], starts[lo]};
   }
-  // many pairs: scan the item counts again
-  int run = 0;
+  // many pairs: scan the prefixes again
+  int crun = 0, irun = 0;
   __syncthreads();
-  if (threadIdx.x == 0) { scratch[8] = -1; scratch[9] = 0; }
+  if (threadIdx.x == 0) scratch[8] = -1;
   for (int b0 = 0; b0 < P; b0 += kThreads) {
     const int pr = b0 + (int)threadIdx.x;
-    const int cnt = pr < P ? ceil_div(pair_tiles(p, pr), pl.tpi) : 0;
-    int tot;
-    const int my0 = run + block_excl_scan(cnt, scratch, &tot);
-    if (pr < P && item >= my0 && item < my0 + cnt) { scratch[8] = pr; scratch[9] = my0; }
-    run += tot;
+    const int t = pr < P ? pair_tiles(p, pr) : 0;
+    int ctot, itot;
+    const int cex = crun + block_excl_scan(pair_cost(t), scratch, &ctot);
+    const int iex = irun + block_excl_scan(pair_items(cex + kPieceCost, t, pl.U), scratch, &itot);
+    if (t > 0 && x >= cex && x < cex + pair_cost(t)) {
+      scratch[8] = pr;
+      scratch[9] = cex;
+      scratch[10] = cex + pair_cost(t);
+      scratch[11] = iex;
+    }
+    crun += ctot;
+    irun += itot;
   }
   __syncthreads();
-  return make_int2(scratch[8], scratch[9]);
+  return PairAt{scratch[8], scratch[9], scratch[10], scratch[11]};
 }
 
 // XOR key of token tau's 16-byte pieces inside each 128-byte group of its LDS
@@ -324,31 +335,39 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
   __shared__ int tbl[kTableCache];
   __shared__ int starts[kPlanPairsLds + 1];
+  __shared__ int cstart[kPlanPairsLds + 1];
   __shared__ int scratch[16];
 
   const int S = p.S, I = p.I;
   const int bs_mask = (1 << p.bs_log2) - 1;
   const float c = p.c_log2;
 
-  const Plan pl = make_plan(p, starts, scratch);
+  const Plan pl = make_plan(p, starts, cstart, scratch);
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
 
-  // Work units = (item, row group), walked by the persistent grid.  The row
-  // groups of one item get unit ids congruent mod 8, and unit u runs on
-  // workgroup u mod gridDim (a multiple of 8): the same XCD and its L2.
-  const int units = ceil_div(pl.n_items, 8) * 8 * G;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    int item, rg;
-    if (G == 1) {
-      item = u;
-      rg = 0;
-    } else {
-      const int x = u & 7, k8 = u >> 3;
-      rg = k8 % G;
-      item = (k8 / G) * 8 + x;
-    }
-    if (item >= pl.n_items) continue;
+  // Workgroup -> (slot, row group): the row groups of slot j run on XCD j % 8
+  // (workgroup i runs on XCD i % 8), walking the same KV tiles at the same
+  // time, so that XCD's L2 serves the repeats.  With 32 % G != 0 the last
+  // 32 % G workgroups of each XCD stay idle.
+  const int k8 = blockIdx.x >> 3;
+  if (k8 >= G * (32 / G)) return;
+  const int slot = 8 * (k8 / G) + (int)(blockIdx.x & 7);
+  const int rg = k8 % G;
+  const int x_end = min((slot + 1) * pl.W, pl.T);
+  for (int x = slot * pl.W; x < x_end;) {
+    // The next item of this slot's cost range: the part of the pair at x that
+    // lies in x's cell (the pair's leading kPieceCost units hold no tiles).
+    const PairAt pa = pair_at(p, pl, x, starts, cstart, scratch);
+    const int tx0 = pa.cstart + kPieceCost;  // cost position of the pair's first tile
+    x = max(x, tx0);
+    if (x >= x_end) break;
+    const int piece_end = min(min(x_end, pa.cend), (x / pl.U + 1) * pl.U);
+    const int item = pa.istart + x / pl.U - tx0 / pl.U;
+    const int tile0 = x - tx0;
+    const int tile1 = piece_end - tx0;
+    x = piece_end;
+    if (item >= p.items_cap) continue;  // never with the host's sizing
     // Lane-dependent values are recomputed per unit from an opaque copy of the
     // thread id, so that none is hoisted out of the unit loop and kept live
     // (and spilled) across the walks: recomputing them is cheaper.
@@ -367,14 +386,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int dma_tau = wave * 8 + (lane_o >> 3);
     const int dma_swz = ((lane_o & 7) ^ piece_swizzle(dma_tau)) * 16;
 
-    const int2 pk = find_pair(p, pl, item, starts, scratch);
-    const int pair = pk.x;
+    const int pair = pa.pair;
     const int b = pair / p.shard_count;
     const int s = p.shard_begin + pair % p.shard_count;
     const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
     const int n_bs = local_len(L, S, I, s);
-    const int tile0 = (item - pk.y) * pl.tpi;
-    const int tile1 = min(tile0 + pl.tpi, ceil_div(n_bs, kTile));
     const int nt = tile1 - tile0;
 
     // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     // The previous unit is done with the ring and the table window.
     __syncthreads();
 
-    // Block-table window of this item (fits kTableCache by the choice of tpi_max).
+    // Block-table window of this item (fits kTableCache: U <= tpi_max).
     const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
     const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
     const int span = blk_hi - blk_lo + 1;

@@ -65,16 +65,23 @@ inline int32_t max_tiles_per_item(int32_t S, int32_t I, int32_t block_size) {
   return lo;
 }
 
-// Tiles per item for a launch: spread `total_tiles` over the item slots that
-// remain after every (request, shard) pair has had one slot for its rounding.
-MLA_HD int32_t tiles_per_item(int32_t total_tiles, int32_t items_cap, int32_t pairs,
-                              int32_t tpi_min, int32_t tpi_max) {
-  int32_t free_slots = items_cap - pairs;
-  if (free_slots < 1) free_slots = 1;
-  int32_t tpi = ceil_div(total_tiles > 0 ? total_tiles : 1, free_slots);
-  if (tpi < tpi_min) tpi = tpi_min;
-  if (tpi > tpi_max) tpi = tpi_max;
-  return tpi;
+// Cost, in tiles' worth of time, of one more item: the prologue that loads
+// its block-table window, q and first tiles, and the epilogue that writes
+// its partial.  The even split charges it once per (request, shard) pair.
+constexpr int kPieceCost = 8;
+
+// Cost units of a pair with `tiles` tiles (a pair without tokens costs nothing).
+MLA_HD int32_t pair_cost(int32_t tiles) { return tiles > 0 ? tiles + kPieceCost : 0; }
+
+// Items of a pair whose tiles occupy cost positions [x0, x0 + tiles): the
+// cells of U units they touch.
+MLA_HD int32_t pair_items(int32_t x0, int32_t tiles, int32_t U) {
+  return tiles > 0 ? (x0 + tiles - 1) / U - x0 / U + 1 : 0;
 }
+
+// Workgroup slots per row group: slot j of every row group runs on XCD j % 8
+// (workgroup i runs on XCD i % 8), so the row groups of one slot share the
+// KV tiles they read through that XCD's L2.
+MLA_HD int32_t plan_slots(int32_t row_groups) { return 8 * (32 / row_groups); }
 
 }  // namespace mla

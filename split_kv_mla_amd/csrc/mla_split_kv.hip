@@ -17,11 +17,6 @@ namespace {
 
 using mla::ceil_div;
 
-// Workgroups the partial kernel keeps busy: one per compute unit of an MI355X
-// (256 CUs), each holding one 4-wave workgroup (the LDS ring and the
-// accumulators allow no second one).
-constexpr int kTargetWorkgroups = mla::kNumCUs;
-
 // Item partial slots are sized for float32; the partial kernel stores a row as
 // fp16 (in the slot's first half) when that is accurate enough (see
 // kHalfPartialMax) and records the choice per row.
@@ -47,38 +42,43 @@ int check_args(const mla_decode_args* a) {
   if ((int64_t)a->num_shards * a->interleave > (1 << 24)) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)a->num_blocks * a->block_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)a->batch * a->num_shards > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  // the device plan's cost axis (tiles plus kPieceCost per pair) stays well inside int32
+  const int64_t cost_bound = (int64_t)a->batch *
+      ((int64_t)a->max_blocks_per_seq * a->block_size / mla::kTile + (int64_t)a->num_shards * (1 + mla::kPieceCost));
+  if (cost_bound > (1 << 30)) return MLA_ERR_UNSUPPORTED;
   if (mla::max_tiles_per_item(a->num_shards, a->interleave, a->block_size) < 1) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
 struct Plan {
-  int32_t pairs, row_groups, items_cap, tpi_min, tpi_max, slots_per_wave;
+  int32_t pairs, row_groups, items_cap, tpi_max, slots;
   size_t plan_bytes, lse_bytes, fmt_bytes, o_bytes;
   size_t total() const { return plan_bytes + lse_bytes + fmt_bytes + o_bytes; }
 };
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Capacity of the item plan: enough slots that the device-side split, whatever
-// the lengths, never produces more items than the grid has workgroups for.
+// Capacity of the item plan.  The device splits the launch's cost axis (tiles
+// plus kPieceCost per non-empty pair) into `slots` ranges of m cells of U
+// tiles, m = ceil(ceil(T / slots) / tpi_max); the cells cover at most
+// slots * m positions and each pair adds at most one item to the cells it
+// touches, so slots * m + pairs items always fit.  T is at most the cost of
+// every request filling its block table.
 Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count) {
   Plan p{};
   const int32_t rows_total = a->rows * a->heads;
   p.pairs = a->batch * shard_count;
   p.row_groups = ceil_div(rows_total, mla::kRowsPerGroup);
   p.tpi_max = mla::max_tiles_per_item(a->num_shards, a->interleave, a->block_size);
-  p.tpi_min = 1;
+  p.slots = mla::plan_slots(p.row_groups);
   const int32_t cap_tokens = a->max_blocks_per_seq * a->block_size;
   int64_t cap_tiles = 0;
   for (int32_t s = shard_begin; s < shard_begin + shard_count; ++s)
     cap_tiles += ceil_div(mla::local_len(cap_tokens, a->num_shards, a->interleave, s), mla::kTile);
-  cap_tiles *= a->batch;
-  // The device plan produces at most pairs + 4 waves of items, or, when the
-  // table window caps the item length, ceil(tiles / tpi_max) + pairs items.
-  p.slots_per_wave = std::max(1, kTargetWorkgroups / p.row_groups);
-  const int64_t need = (cap_tiles + p.tpi_max - 1) / p.tpi_max + p.pairs;
-  const int64_t waves = (int64_t)p.pairs + 4 * (int64_t)p.slots_per_wave;
-  p.items_cap = (int32_t)std::max<int64_t>(need, waves);
+  const int64_t cap_cost = (cap_tiles + mla::kPieceCost) * a->batch;
+  const int64_t wmin = std::max<int64_t>(1, (cap_cost + p.slots - 1) / p.slots);
+  const int64_t m = (wmin + p.tpi_max - 1) / p.tpi_max;
+  p.items_cap = (int32_t)std::min<int64_t>((int64_t)p.slots * m + p.pairs, INT32_MAX);
   p.plan_bytes = round_up(sizeof(int32_t) * (size_t)(p.pairs + 2), 256);
   p.lse_bytes = round_up(sizeof(float) * (size_t)p.items_cap * rows_total, 256);
   p.fmt_bytes = round_up((size_t)p.items_cap * rows_total, 256);
@@ -114,9 +114,8 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   p.shard_count = shard_count;
   p.pairs = pl.pairs;
   p.items_cap = pl.items_cap;
-  p.tpi_min = pl.tpi_min;
   p.tpi_max = pl.tpi_max;
-  p.slots_per_wave = pl.slots_per_wave;
+  p.slots = pl.slots;
   p.c_log2 = a->softmax_scale * mla::kLog2e;
   p.causal = a->causal ? 1 : 0;
   return p;

@@ -49,7 +49,7 @@ def test_workspace_sizing():
     a = _args()
     n = m.mla_workspace_bytes(a)
     items, groups = m.mla_plan_capacity(a)
-    assert groups == 1 and items >= 2 * 8 + 1
+    assert groups == 1 and items >= 2 * 8 + 256
     rows = a.rows * a.heads
     assert n >= items * rows * 512 * 2 + items * rows * 4
     a4 = _args(R=4)
@@ -61,25 +61,86 @@ def test_workspace_sizing():
         assert m.mla_workspace_bytes(_args(**bad)) == 0, bad
 
 
+PIECE_COST = 8  # kPieceCost of the device plan
+
+
+def _tpi_max(S, I, bs):
+    span = lambda t: ((t * 32 + I - 1) // I + 1) * S * I // bs + 2
+    t = 1
+    while span(t + 1) <= 2048:
+        t += 1
+    return t
+
+
+def _even_split(tiles, slots, tpi_max):
+    """Model of the device plan: pairs end to end on a cost axis (PIECE_COST +
+    tiles each), cut into `slots` equal ranges of m cells of U units.
+    Returns (U, W, T, pieces) with pieces = (slot, pair, item, tile0, tile1)."""
+    costs = [t + PIECE_COST if t > 0 else 0 for t in tiles]
+    T = sum(costs)
+    wmin = max(1, -(-T // slots))
+    m = -(-wmin // tpi_max)
+    U = -(-wmin // m)
+    W = m * U
+    cst, ist, c, i = [], [], 0, 0
+    for t, k in zip(tiles, costs):
+        cst.append(c)
+        ist.append(i)
+        if t > 0:
+            x0 = c + PIECE_COST
+            i += (x0 + t - 1) // U - x0 // U + 1
+        c += k
+    pieces = []
+    for slot in range(slots):
+        x, x_end = slot * W, min((slot + 1) * W, T)
+        while x < x_end:
+            pr = max(j for j in range(len(tiles)) if cst[j] <= x and costs[j] > 0)
+            tx0 = cst[pr] + PIECE_COST
+            x = max(x, tx0)
+            if x >= x_end:
+                break
+            end = min(x_end, cst[pr] + costs[pr], (x // U + 1) * U)
+            pieces.append((slot, pr, ist[pr] + x // U - tx0 // U, x - tx0, end - tx0))
+            x = end
+    return U, W, T, pieces
+
+
+def test_even_split_covers_every_tile_once_with_balanced_slots():
+    rng = __import__("random").Random(5)
+    for _ in range(40):
+        P = rng.choice([1, 3, 8, 64, 200])
+        tiles = [rng.choice([0, 1, 2, 7, 33, 469, 2000, rng.randrange(1, 5000)]) for _ in range(P)]
+        slots = rng.choice([256, 128, 80, 64, 32])
+        tpi_max = rng.choice([7, 64, 512, 4000])
+        U, W, T, pieces = _even_split(tiles, slots, tpi_max)
+        seen = {}
+        for slot, pr, item, t0, t1 in pieces:
+            assert 0 <= t0 < t1 <= tiles[pr] and t1 - t0 <= U <= tpi_max
+            for t in range(t0, t1):
+                assert (pr, t) not in seen
+                seen[(pr, t)] = item
+        assert len(seen) == sum(tiles)
+        # items are numbered densely per pair, in tile order
+        n_items = len({p[2] for p in pieces})
+        assert n_items == len(pieces)
+        assert sorted(p[2] for p in pieces) == list(range(n_items))
+        # every slot's cost (its tiles, plus PIECE_COST for each pair it starts) is at most W
+        for s in range(slots):
+            mine = [p for p in pieces if p[0] == s]
+            assert sum(t1 - t0 for _, _, _, t0, t1 in mine) <= W
+
+
 def test_plan_capacity_covers_longest_requests():
-    """Items needed when every request fills the table never exceed the capacity."""
-    for S, I, bs, maxb in [(8, 1, 64, 2048), (8, 16, 64, 2048), (3, 5, 16, 100), (1, 1, 1, 4000),
-                           (16, 64, 128, 1024)]:
-        a = _args(B=3, S=S, I=I, bs=bs, max_blocks=maxb)
-        cap, _ = m.mla_plan_capacity(a)
+    """Items of the device plan when every request fills its table never exceed the capacity."""
+    for S, I, bs, maxb, R in [(8, 1, 64, 2048, 1), (8, 16, 64, 2048, 4), (3, 5, 16, 100, 1), (1, 1, 1, 4000, 2),
+                              (16, 64, 128, 1024, 3)]:
+        a = _args(B=3, R=R, S=S, I=I, bs=bs, max_blocks=maxb)
+        cap, groups = m.mla_plan_capacity(a)
+        slots = 8 * (32 // groups)
         L = maxb * bs
-        tiles = [(((L // (S * I)) * I + min(I, max(0, L % (S * I) - s * I))) + 31) // 32 for s in range(S)]
-        total = 3 * sum(tiles)
-        pairs = 3 * S
-        # the kernel's choice: ceil(total / (cap - pairs)) clamped to the table-window limit
-        from math import ceil
-        span_units = lambda t: (t * 32 + I - 1) // I + 1
-        tmax = 1
-        while (span_units(tmax + 1) * S * I) // bs + 2 <= 2048:
-            tmax += 1
-        tpi = min(max(1, ceil(total / max(1, cap - pairs))), tmax)
-        items = 3 * sum((t + tpi - 1) // tpi for t in tiles)
-        assert items <= cap, (S, I, bs, maxb, items, cap)
+        tiles = [(((L // (S * I)) * I + min(I, max(0, L % (S * I) - s * I))) + 31) // 32 for s in range(S)] * 3
+        U, W, T, pieces = _even_split(tiles, slots, _tpi_max(S, I, bs))
+        assert len(pieces) <= cap, (S, I, bs, maxb, len(pieces), cap)
 
 
 def test_bad_arguments_return_errors_without_launching():
