@@ -93,7 +93,8 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive prefix over the workgroup's 256 threads; `total` gets the sum.
+// Exclusive prefix over the workgroup's NT threads; `total` gets the sum.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
   const int incl = wave_incl_scan(v);
   const int w = threadIdx.x >> 6;
@@ -101,7 +102,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) 
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const int x = scratch[i];
     off += (i < w) ? x : 0;
     tot += x;
@@ -111,24 +112,22 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) 
   return off + incl - v;
 }
 
-// OR of a flag over the 256-thread workgroup, with a barrier: a wave vote,
-// one LDS word per wave (slots[0..3] of a caller-provided LDS array).  Cheaper
-// than the generic block vote, which reads the dispatch packet for the block
-// shape.
+// OR of a flag over a workgroup of NW wavefronts, with a barrier: a wave vote,
+// one LDS word per wave (slots[0..NW-1] of a caller-provided LDS array).
+// Cheaper than the generic block vote, which reads the dispatch packet for
+// the block shape.
 // `wave` and `lane` are the caller's (wave-uniform / per-lane) indices.
+template <int NW = kThreads / 64>
 __device__ __forceinline__ bool block_any(bool v, int* slots, int wave, int lane) {
   const bool wv = __any(v);
   if (lane == 0) slots[wave] = wv ? 1 : 0;
   __syncthreads();
-  const bool r = (slots[0] | slots[1] | slots[2] | slots[3]) != 0;
+  int o = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) o |= slots[i];
+  const bool r = o != 0;
   __syncthreads();  // the slots can be reused after this
   return r;
-}
-
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
-  return v;
 }
 
 // Request length with out-of-range values treated as empty (the combine
@@ -146,6 +145,7 @@ __device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
   return ceil_div(local_len(L, p.S, p.I, s), kTile);
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -154,7 +154,7 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
   __syncthreads();
   int t = 0;
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) t += scratch[i];
+  for (int i = 0; i < NT / 64; ++i) t += scratch[i];
   return t;
 }
 
@@ -174,17 +174,18 @@ struct Plan {
 // the same cost give or take one cell's rounding.  Cost and item prefixes per
 // pair go to `cstart` / `starts` (LDS) when the pairs fit, and workgroup 0
 // publishes the item prefixes with the item total and U for the combine.
+template <int NT = kThreads>
 __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* scratch) {
   const int P = p.pairs;
-  const bool in_reg = P <= kThreads;
+  const bool in_reg = P <= NT;
   const int my_t = (in_reg && (int)threadIdx.x < P) ? pair_tiles(p, threadIdx.x) : 0;
   int T = 0;
   if (in_reg) {
-    T = block_sum(pair_cost(my_t), scratch);
+    T = block_sum<NT>(pair_cost(my_t), scratch);
   } else {
-    for (int b0 = 0; b0 < P; b0 += kThreads) {
+    for (int b0 = 0; b0 < P; b0 += NT) {
       const int pr = b0 + (int)threadIdx.x;
-      T += block_sum(pr < P ? pair_cost(pair_tiles(p, pr)) : 0, scratch);
+      T += block_sum<NT>(pr < P ? pair_cost(pair_tiles(p, pr)) : 0, scratch);
     }
   }
   const int wmin = max(1, ceil_div(T, p.slots));
@@ -194,12 +195,12 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
   const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
   int crun = 0, irun = 0;
   if (keep || publish) {
-    for (int b0 = 0; b0 < P; b0 += kThreads) {
+    for (int b0 = 0; b0 < P; b0 += NT) {
       const int pr = b0 + (int)threadIdx.x;
       const int t = in_reg ? my_t : (pr < P ? pair_tiles(p, pr) : 0);
       int ctot, itot;
-      const int cex = crun + block_excl_scan(pr < P ? pair_cost(t) : 0, scratch, &ctot);
-      const int iex = irun + block_excl_scan(pr < P ? pair_items(cex + kPieceCost, t, U) : 0, scratch, &itot);
+      const int cex = crun + block_excl_scan<NT>(pr < P ? pair_cost(t) : 0, scratch, &ctot);
+      const int iex = irun + block_excl_scan<NT>(pr < P ? pair_items(cex + kPieceCost, t, U) : 0, scratch, &itot);
       if (pr < P) {
         if (keep) {
           cstart[pr] = cex;
@@ -233,6 +234,7 @@ struct PairAt {
 };
 
 // The non-empty pair whose cost range holds cost position x (0 <= x < T).
+template <int NT = kThreads>
 __device__ PairAt pair_at(const DecodeParams& p, const Plan& pl, int x, const int* starts, const int* cstart,
                           int* scratch) {
   const int P = p.pairs;
@@ -248,12 +250,12 @@ __device__ PairAt pair_at(const DecodeParams& p, const Plan& pl, int x, const in
   int crun = 0, irun = 0;
   __syncthreads();
   if (threadIdx.x == 0) scratch[8] = -1;
-  for (int b0 = 0; b0 < P; b0 += kThreads) {
+  for (int b0 = 0; b0 < P; b0 += NT) {
     const int pr = b0 + (int)threadIdx.x;
     const int t = pr < P ? pair_tiles(p, pr) : 0;
     int ctot, itot;
-    const int cex = crun + block_excl_scan(pair_cost(t), scratch, &ctot);
-    const int iex = irun + block_excl_scan(pair_items(cex + kPieceCost, t, pl.U), scratch, &itot);
+    const int cex = crun + block_excl_scan<NT>(pair_cost(t), scratch, &ctot);
+    const int iex = irun + block_excl_scan<NT>(pair_items(cex + kPieceCost, t, pl.U), scratch, &itot);
     if (t > 0 && x >= cex && x < cex + pair_cost(t)) {
       scratch[8] = pr;
       scratch[9] = cex;
@@ -398,7 +400,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const bool row_ok = row < p.rows_total;
     const int r = row_ok ? row / p.H : 0;
     const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
-    const int lim_min = wave_min(lim);
 
     // The previous unit is done with the ring and the table window.
     __syncthreads();
@@ -687,6 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       walk(Full{}, false, unused);
       wait_vmcnt<0>();
       m_ref = m_exact;
+      __syncthreads();  // every wavefront is done with the ring before it stages rows
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

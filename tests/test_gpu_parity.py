@@ -95,6 +95,19 @@ def test_outliers_and_large_q():
     _check_full(w, "outliers")
 
 
+def test_late_dominant_token_takes_slow_path():
+    """A token far past the first tile scores ~100 binary orders above that
+    tile's maximum: the running denominator passes 2^96 and the kernel redoes
+    the item against the exact maximum (its rare slow path)."""
+    w = build("late_peak", [1000, 600], R=2, H=32, num_shards=2, interleave=1, seed=79)
+    bs = w.block_size
+    for b, t in ((0, 901), (1, 590)):
+        blk = w.block_table[b, t // bs]
+        w.kv_bits[blk, t % bs, :] = 0x3F80  # every column 1.0
+    w.q_bits[...] = 0x4000  # every q element 2.0: that token scores 1152 * scale = 83 nats
+    _check_full(w, "late_peak")
+
+
 def test_tiny_config():
     _check_full(workloads.tiny(), "tiny_config")
 
