@@ -320,6 +320,25 @@ __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
+// S^T += K Q^T with the accumulator in VGPRs.  The compiler gives every
+// matrix product of the partial kernel the AGPR form once the 256-register PV
+// accumulator fills the AGPRs, and then evicts a block of that accumulator
+// around each score product; written as assembly the score chain stays in
+// VGPRs.  The chain's products follow each other directly (the hardware
+// forwards the accumulator, as in the compiler's own chains), the first takes
+// an inline zero accumulator, and mfma_vgpr_done separates the last product
+// from any VALU read of its result by the 12 wait states that the compiler
+// itself inserts after a VGPR-form 32x32x16 product.  Each product is a
+// scheduling fence for memory operations, so operand reads stay in the order
+// the caller writes them.
+__device__ __forceinline__ void mfma_vgpr_first(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_vgpr_next(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_vgpr_done(f32x16& s) { asm volatile("s_nop 11" : "+v"(s)); }
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -585,20 +604,20 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       };
       // S^T of the tile in `buf` on its own (the first tile of the walk).
       auto qk_alone = [&](const char* buf) {
-        f32x16 sc = f32x16{};
+        // the K reads run kAhead products ahead of their use (the products'
+        // memory clobber keeps the reads where they are written)
+        constexpr int kAhead = 6;
+        f32x16 sc;
         bf16x8 kf[36];
 #pragma unroll
-        for (int db = 0; db < 36; ++db) kf[db] = k_frag(buf, db);
+        for (int db = 0; db < kAhead; ++db) kf[db] = k_frag(buf, db);
 #pragma unroll
-        for (int db = 0; db < 36; ++db) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[db], qf[db], sc, 0, 0, 0);
-        constexpr int kAhead = 6;
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-        for (int i = 0; i < 36 - kAhead; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int db = 0; db < 36; ++db) {
+          if (db == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
+          else mfma_vgpr_next(sc, kf[db], qf[db]);
+          if (db + kAhead < 36) kf[db + kAhead] = k_frag(buf, db + kAhead);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        mfma_vgpr_done(sc);
         return sc;
       };
       // PV product i of a tile (64 per tile): fragment i/2, P_hi for even i, P_lo for odd.

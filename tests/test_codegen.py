@@ -1,0 +1,86 @@
+"""Device assembly of the library (built here for gfx950, no GPU needed).
+
+The partial kernel leans on three facts that the compiler does not check for
+it, because they involve inline assembly:
+* M0 is written only by the LDS-DMA helpers, each time right before their load;
+* the score products written as assembly accumulate in VGPRs, and nothing
+  reads their result before 12 wait states have passed (the spacing the
+  compiler itself uses after a VGPR-form 32x32x16 product);
+* no packed fp32 arithmetic appears in the generated code.
+"""
+
+import os
+import re
+import tempfile
+
+import pytest
+
+from split_kv_mla_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def asm():
+    if not os.path.exists(B.hipcc()):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        path = B.assembly(os.path.join(d, "mla.s"))
+        return open(path).read().split("\n")
+
+
+def _code(line):
+    return line.split(";")[0].strip()
+
+
+def test_m0_written_only_by_the_lds_dma_helpers(asm):
+    seen = 0
+    for i, line in enumerate(asm):
+        x = _code(line)
+        if not re.search(r"\bm0\b", x):
+            continue
+        assert re.fullmatch(r"s_mov_b32 m0, s\d+", x), f"line {i + 1}: {x}"
+        nxt = [_code(y) for y in asm[i + 1:i + 3]]
+        assert nxt[0] == "s_nop 0" and nxt[1].startswith("global_load_lds_dword"), f"line {i + 1}: {nxt}"
+        seen += 1
+    assert seen > 0
+
+
+def _regs(text):
+    out = set()
+    for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", text):
+        out |= set(range(int(a), int(b) + 1))
+    out |= {int(a) for a in re.findall(r"\bv(\d+)\b", text)}
+    return out
+
+
+def test_vgpr_form_products_are_read_after_12_wait_states(asm):
+    checked = 0
+    for i, line in enumerate(asm):
+        m = re.match(r"\s*v_mfma_\w+\s+v\[(\d+):(\d+)\],", line)
+        if not m:
+            continue
+        dst = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        checked += 1
+        waits = 0
+        for j in range(i + 1, min(len(asm), i + 400)):
+            x = _code(asm[j])
+            if not x or (x.startswith(".") and not x.endswith(":")):
+                continue
+            assert not x.endswith(":"), f"line {i + 1}: result crosses a label before its use"
+            n = re.match(r"s_nop\s+(\d+)", x)
+            if n:
+                waits += int(n.group(1)) + 1
+                continue
+            if _regs(x) & dst:
+                chain = re.match(r"v_mfma_\w+\s+v\[(\d+):(\d+)\],.*v\[(\d+):(\d+)\]$", x)
+                if chain and set(range(int(chain.group(1)), int(chain.group(2)) + 1)) == dst \
+                        and set(range(int(chain.group(3)), int(chain.group(4)) + 1)) == dst:
+                    break  # the next product of the chain accumulates in place
+                assert waits >= 12, f"line {i + 1} -> {j + 1}: {x} after {waits} wait states"
+                break
+            waits += 1
+    assert checked > 0
+
+
+def test_no_packed_fp32_instructions(asm):
+    hits = [i + 1 for i, line in enumerate(asm) if re.search(r"\bv_pk_(add|mul|fma)_f32\b", _code(line))]
+    assert not hits, hits[:10]
