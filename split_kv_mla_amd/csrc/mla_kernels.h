@@ -418,7 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
     const bool row_ok = row < p.rows_total;
     const int r = row_ok ? row / p.H : 0;
-    const int lim = local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s);
+    // Local tokens the row sees, cut at the item's end: the walk also scores the
+    // stage after the item's last tile, and this masks all of it.
+    const int lim = min(local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s), tile1 * kTile);
 
     // The previous unit is done with the ring and the table window.
     __syncthreads();
@@ -557,8 +559,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       const char* next_src = tile_src(tile0 + kStages - 1);
       float m_walk = -INFINITY;
 
-      // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4))
-      // -> P^T fragments, or the running maximum.
       // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4)):
       // masks the tokens at or past the row's end and returns the softmax
       // reference, or (kMaxOnly) folds the row maximum into m_walk.
@@ -585,13 +585,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // P_lo, both bf16: a single bf16 P would cost up to 2^-8 of relative
       // weight per token, too much for rows of a few tokens or with outlier
       // values; the pair leaves a residual of at most 2^-16 p.
-      auto make_p1 = [&](PFrag& pf, const f32x16& sc, float msafe, int j) {
-        const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 + j], c, -msafe));
-        l_run += x;
-        const __bf16 hi = (__bf16)x;
-        pf.hi[1][j] = hi;
-        pf.lo[1][j] = (__bf16)(x - (float)hi);
-      };
       auto make_p = [&](PFrag& pf, const f32x16& sc, float msafe, int kb) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -626,59 +619,90 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);
       };
 
-      for (int k = 0; k < nt; ++k) {
-        // tile k resident: the prologue always fills kStages-1 stages, so the
-        // younger loads in flight are min(2, nt-1-k), or the spare re-reads
-        // when the item has fewer than kStages-1 tiles (Q, loaded between
-        // tiles 0 and 1, is resident with tile 0)
-        const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
-        if (younger >= 2) wait_vmcnt<18>();
-        else if (younger == 1) wait_vmcnt<9>();
-        else wait_vmcnt<0>();
-        // every wavefront is past tile k-1: its stage takes tile k+3
-        lds_barrier();
-        if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
-        next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
-        const char* buf = ring + (k % kStages) * kTileBytes;
-        f32x16 sc = qk_alone(buf);
-        const float msafe = prep(sc, k);
-        if constexpr (!kMaxOnly) {
-          // O^T[dim][row] += V^T[dim][token] P^T[token][row]; the second half of
-          // P is formed under the first half's products
-          PFrag pf;
-          make_p(pf, sc, msafe, 0);
-          bf16x8 vf[32];
-          // first 12 products (6 fragments) with their reads 6 ahead ...
-#pragma unroll
-          for (int f = 0; f < 9; ++f) vf[f] = v_frag(buf, f);
-#pragma unroll
-          for (int i = 0; i < 12; ++i) pv_mfma(vf, pf, i);
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-          for (int i = 0; i < 6; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          // ... then the second half of P while they run in the matrix pipe ...
-          make_p(pf, sc, msafe, 1);
-          __builtin_amdgcn_sched_barrier(0);
-          // ... then the other 52 products
-#pragma unroll
-          for (int f = 9; f < 32; ++f) vf[f] = v_frag(buf, f);
-#pragma unroll
-          for (int i = 12; i < 64; ++i) pv_mfma(vf, pf, i);
-#pragma unroll
-          for (int i = 0; i < 23; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        }
-      }
       if constexpr (kMaxOnly) {
+        for (int k = 0; k < nt; ++k) {
+          // tile k resident: the prologue always fills kStages-1 stages, so the
+          // younger loads in flight are min(2, nt-1-k), or the spare re-reads
+          // when the item has fewer than kStages-1 tiles
+          const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
+          if (younger >= 2) wait_vmcnt<18>();
+          else if (younger == 1) wait_vmcnt<9>();
+          else wait_vmcnt<0>();
+          // every wavefront is past tile k-1: its stage takes tile k+3
+          lds_barrier();
+          if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
+          next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
+          f32x16 sc = qk_alone(ring + (k % kStages) * kTileBytes);
+          prep(sc, k);
+        }
         m_ref = m_walk;
       } else {
+        // Tile 0's scores and P first; then iteration k forms tile k+1's
+        // scores in the VGPR chain while tile k's PV products run on the AGPR
+        // accumulator, and tile k+1's P under the last of those products, so
+        // the matrix pipe does not wait for the softmax.
+        wait_vmcnt<18>();  // tile 0 (tiles 1 and 2 in flight)
+        lds_barrier();
+        PFrag pf;
+        {
+          f32x16 sc = qk_alone(ring);
+          const float msafe = prep(sc, 0);
+          make_p(pf, sc, msafe, 0);
+          make_p(pf, sc, msafe, 1);
+        }
+        for (int k = 0; k < nt; ++k) {
+          const bool more = k + 1 < nt;
+          if (more) {
+            // tile k+1 resident: the loads issued so far are the prologue's
+            // three plus one per earlier iteration that still had a tile to load
+            const int younger = 3 + max(0, min(k, nt - kStages + 1)) - (k + 2);
+            if (younger >= 1) wait_vmcnt<9>();
+            else wait_vmcnt<0>();
+          }
+          // every wavefront is past iteration k-1 (tile k-1's products): its
+          // stage takes tile k+3
+          lds_barrier();
+          if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
+          next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
+          const char* buf = ring + (k % kStages) * kTileBytes;
+          const char* nbuf = ring + ((k + 1) % kStages) * kTileBytes;
+          // O^T[dim][row] += V^T[dim][token] P^T[token][row]: product i uses
+          // fragment i/2 (read kVAhead fragments ahead), P_hi for even i, P_lo for odd
+          constexpr int kVAhead = 2;
+          bf16x8 vf[32];
+#pragma unroll
+          for (int f = 0; f < kVAhead; ++f) vf[f] = v_frag(buf, f);
+          auto pv_step = [&](int i) {
+            pv_mfma(vf, pf, i);
+            if ((i & 1) && (i >> 1) + kVAhead < 32) vf[(i >> 1) + kVAhead] = v_frag(buf, (i >> 1) + kVAhead);
+          };
+          {
+            // the next tile's 36 score products alternate with this tile's
+            // first 36 PV products; K reads run kAhead products ahead.  In the
+            // last iteration the next stage holds no tile of the item: every
+            // score there is masked, so its P is zero and adds nothing.
+            constexpr int kAhead = 4;
+            f32x16 sc;
+            bf16x8 kf[36];
+#pragma unroll
+            for (int db = 0; db < kAhead; ++db) kf[db] = k_frag(nbuf, db);
+#pragma unroll
+            for (int i = 0; i < 36; ++i) {
+              if (i == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
+              else mfma_vgpr_next(sc, kf[i], qf[i]);
+              if (i + kAhead < 36) kf[i + kAhead] = k_frag(nbuf, i + kAhead);
+              pv_step(i);
+            }
+            mfma_vgpr_done(sc);
+            const float msafe = prep(sc, k + 1);
+            PFrag pn;
+            make_p(pn, sc, msafe, 0);
+            make_p(pn, sc, msafe, 1);
+#pragma unroll
+            for (int i = 36; i < 64; ++i) pv_step(i);
+            pf = pn;
+          }
+        }
         // a score far above the reference pushes the denominator past 2^96 (or to
         // inf/NaN): then the walk is redone from the exact maximum
         overflow |= !(l_run < kSlackValue);
