@@ -668,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           const char* nbuf = ring + ((k + 1) % kStages) * kTileBytes;
           // O^T[dim][row] += V^T[dim][token] P^T[token][row]: product i uses
           // fragment i/2 (read kVAhead fragments ahead), P_hi for even i, P_lo for odd
-          constexpr int kVAhead = 2;
+          constexpr int kVAhead = 6;
           bf16x8 vf[32];
 #pragma unroll
           for (int f = 0; f < kVAhead; ++f) vf[f] = v_frag(buf, f);
