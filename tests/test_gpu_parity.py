@@ -108,6 +108,48 @@ def test_late_dominant_token_takes_slow_path():
     _check_full(w, "late_peak")
 
 
+@pytest.mark.parametrize("S,I", [(3, 1), (5, 2), (8, 16), (4, 7)])
+def test_zero_query_shard_lse_counts_tokens(S, I):
+    """q = 0: every score is 0, so a shard's LSE is ln(number of its tokens)
+    exactly (-inf for none), which pins the shard map on the device."""
+    lens = [1, 37, 300, 0, 1000]
+    w = build("zeroq", lens, R=2, H=16, num_shards=S, interleave=I, seed=80 + S, block_size=16)
+    w.q_bits[...] = 0
+    _say(f"[parity] zero_query S={S} I={I}")
+    out, lse, lf = _run_split(w)
+    for b, L in enumerate(lens):
+        for r in range(2):
+            n = max(0, L - (1 - r))
+            for s in range(S):
+                cnt = sum(1 for t in range(n) if (t // I) % S == s)
+                got = lse[s, b, r]
+                if cnt == 0:
+                    assert np.all(np.isneginf(got)), (S, I, b, r, s)
+                else:
+                    assert np.all(np.abs(got - math.log(cnt)) <= 1e-5), (S, I, b, r, s, got[:2], math.log(cnt))
+            want = math.log(n) if n else -math.inf
+            assert np.all(np.abs(lf[b, r] - want) <= 1e-5) if n else np.all(np.isneginf(lf[b, r]))
+
+
+def test_spike_token_lands_in_its_shard():
+    """One token far above the rest: the shard whose LSE is largest is the
+    shard of that token, for every position of a small request."""
+    S, I, n = 3, 2, 70
+    base = build("spike", [n], R=1, H=16, num_shards=S, interleave=I, seed=81, block_size=8)
+    base.q_bits[...] = 0x4000  # 2.0
+    m = _lib()
+    kv0 = base.kv_bits.copy()
+    for t in range(n):
+        w = base
+        w.kv_bits = kv0.copy()
+        w.kv_bits[w.block_table[0, t // 8], t % 8, :] = 0x3F80  # 1.0: scores 83 nats above the rest
+        q, kv, bt, sl = to_device(w)
+        _, lse, _ = m.mla_split_decode(q, kv, bt, sl, S, I, w.scale, w.causal)
+        torch.cuda.synchronize()
+        l = lse.cpu().double().numpy()[:, 0, 0, :]  # [S, H]
+        assert np.all(np.argmax(l, axis=0) == (t // I) % S), (t, l[:, 0])
+
+
 def test_tiny_config():
     _check_full(workloads.tiny(), "tiny_config")
 
