@@ -836,19 +836,24 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) 
   return r;
 }
 
-constexpr int kCombineCols = 128;             // output columns per workgroup
-constexpr int kCombineGroups = 16;            // source groups per workgroup
 constexpr int kCombineLdsSources = 2048;      // source LSEs staged in LDS
 
+// One workgroup per (request, row, C-column part); its threads form
+// 2048 / C source groups of C / 8 threads, each thread 8 columns.  Few groups
+// suit few sources per row, many groups many (the host picks C).
+template <int C>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
+  constexpr int kCombineCols = C;
+  constexpr int kCombineGroups = 2048 / C;
+  constexpr int kThreadsPerGroup = C / 8;
   __shared__ float src_lse[kCombineLdsSources];
   __shared__ uint8_t src_fmt[kCombineLdsSources];
   __shared__ f32x4 part[kCombineGroups][kCombineCols / 4];
   __shared__ float red[8];
 
   const int tid = threadIdx.x;
-  const int quarter = blockIdx.x & 3;
-  int unit = blockIdx.x >> 2;
+  const int quarter = blockIdx.x % (kVDim / C);  // which C-column part
+  int unit = blockIdx.x / (kVDim / C);
   const int row = unit % p.rows;
   unit /= p.rows;
   const int b = unit % p.B;
@@ -913,8 +918,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   wsum = block_reduce(wsum, false, red);
 
   // pass 2: weighted sum of this block's 128 columns; thread = (source group, 8 columns)
-  const int sg = tid >> 4;
-  const int col = quarter * kCombineCols + 8 * (tid & 15);
+  const int sg = tid / kThreadsPerGroup;
+  const int col = quarter * kCombineCols + 8 * (tid % kThreadsPerGroup);
   f32x4 acc0 = f32x4{}, acc1 = f32x4{};
   if (!bad && !empty) {
 #pragma unroll 4
@@ -938,8 +943,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       }
     }
   }
-  part[sg][2 * (tid & 15)] = acc0;
-  part[sg][2 * (tid & 15) + 1] = acc1;
+  part[sg][2 * (tid % kThreadsPerGroup)] = acc0;
+  part[sg][2 * (tid % kThreadsPerGroup) + 1] = acc1;
   __syncthreads();
 
   const float qnan = __builtin_nanf("");

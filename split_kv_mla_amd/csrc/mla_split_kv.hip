@@ -127,9 +127,21 @@ int launch_partial(const mla::DecodeParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-int launch_combine(const mla::CombineParams& c, int64_t units, hipStream_t stream) {
-  if (units * 4 > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mla::combine_kernel, dim3((int)(units * 4)), dim3(mla::kThreads), 0, stream, c);
+// `sources` estimates the sources one output row merges: about 8 per thread
+// of a source group, between 4 groups (C = 512: few sources, fewer and
+// wider workgroups) and 32 (C = 64: hundreds of items of one long request).
+int launch_combine(const mla::CombineParams& c, int64_t units, int64_t sources, hipStream_t stream) {
+  int groups = 4;
+  while (groups < 32 && groups * 2 * 8 <= sources) groups *= 2;
+  const int C = 2048 / groups;
+  const int64_t blocks = units * (mla::kVDim / C);
+  if (blocks > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  switch (C) {
+    case 512: hipLaunchKernelGGL(mla::combine_kernel<512>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
+    case 256: hipLaunchKernelGGL(mla::combine_kernel<256>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
+    case 128: hipLaunchKernelGGL(mla::combine_kernel<128>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
+    default: hipLaunchKernelGGL(mla::combine_kernel<64>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -178,7 +190,8 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   c.rows = p.rows_total;
   c.shard_count = shard_count;
   c.mode = mla::kMergeShard;
-  return launch_combine(c, (int64_t)shard_count * a->batch * p.rows_total, s);
+  return launch_combine(c, (int64_t)shard_count * a->batch * p.rows_total,
+                        p.items_cap / ((int64_t)a->batch * shard_count), s);
 }
 
 int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
@@ -201,7 +214,7 @@ int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shar
   c.rows = rows * heads;
   c.shard_count = num_shards;
   c.mode = mla::kCombineShards;
-  return launch_combine(c, (int64_t)batch * c.rows, static_cast<hipStream_t>(stream));
+  return launch_combine(c, (int64_t)batch * c.rows, num_shards, static_cast<hipStream_t>(stream));
 }
 
 int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* workspace,
@@ -232,7 +245,7 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   c.rows = p.rows_total;
   c.shard_count = a->num_shards;
   c.mode = mla::kCombineItems;
-  if ((st = launch_combine(c, (int64_t)a->batch * p.rows_total, s)) != MLA_OK) return st;
+  if ((st = launch_combine(c, (int64_t)a->batch * p.rows_total, p.items_cap / a->batch, s)) != MLA_OK) return st;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
