@@ -56,7 +56,7 @@ constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
 constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
 constexpr int kRowsPerGroup = 4 * kRowsPerWave;   // 128 query rows per workgroup
 constexpr int kNumCUs = 256;                      // MI355X compute units: the persistent grid
-constexpr int kPlanPairsLds = 960;                // per-pair plan prefixes kept in LDS
+constexpr int kPlanPairsLds = 640;                // per-pair plan prefixes and lengths kept in LDS
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 // Item partial rows whose largest |o| is at most this are stored as fp16.
@@ -137,12 +137,17 @@ __device__ __forceinline__ int32_t checked_len(const int32_t* seq_lens, int b, i
   return (L < 0 || L > cap) ? 0 : L;
 }
 
-// Tiles of (request, shard) pair `pr`: its longest row sees the whole request.
-__device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
-  const int b = pr / p.shard_count;
+// Tiles of (request, shard) pair `pr` for a request of L tokens: its longest
+// row sees the whole request.
+__device__ __forceinline__ int32_t pair_tiles_of(const DecodeParams& p, int pr, int32_t L) {
   const int s = p.shard_begin + pr % p.shard_count;
-  const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
   return ceil_div(local_len(L, p.S, p.I, s), kTile);
+}
+__device__ __forceinline__ int32_t pair_len(const DecodeParams& p, int pr) {
+  return checked_len(p.seq_lens, pr / p.shard_count, p.cap_tokens);
+}
+__device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
+  return pair_tiles_of(p, pr, pair_len(p, pr));
 }
 
 template <int NT = kThreads>
@@ -175,8 +180,47 @@ struct Plan {
 // pair go to `cstart` / `starts` (LDS) when the pairs fit, and workgroup 0
 // publishes the item prefixes with the item total and U for the combine.
 template <int NT = kThreads>
-__device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* scratch) {
+__device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* lens, int* scratch) {
   const int P = p.pairs;
+  const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
+  if (P <= 64) {
+    // up to 64 pairs: one wavefront forms the plan with lane scans, the rest
+    // wait at a single barrier
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int32_t L = lane < P ? pair_len(p, lane) : 0;
+      const int t = lane < P ? pair_tiles_of(p, lane, L) : 0;
+      const int cost = pair_cost(t);
+      const int cinc = wave_incl_scan(cost);
+      const int T = __shfl(cinc, 63, 64);
+      const int wmin = max(1, ceil_div(T, p.slots));
+      const int m = ceil_div(wmin, p.tpi_max);
+      const int U = ceil_div(wmin, m);
+      const int cex = cinc - cost;
+      const int items = pair_items(cex + kPieceCost, t, U);
+      const int iinc = wave_incl_scan(items);
+      const int ntot = __shfl(iinc, 63, 64);
+      if (lane < P) {
+        cstart[lane] = cex;
+        starts[lane] = iinc - items;
+        lens[lane] = L;
+        if (publish) p.plan_out[lane] = iinc - items;
+      }
+      if (lane == 0) {
+        cstart[P] = T;
+        starts[P] = ntot;
+        scratch[4] = U;
+        scratch[5] = m;
+        if (publish) {
+          p.plan_out[P] = ntot;
+          p.plan_out[P + 1] = U;
+        }
+      }
+    }
+    __syncthreads();
+    const int U = scratch[4];
+    return Plan{U, scratch[5] * U, cstart[P], starts[P]};
+  }
   const bool in_reg = P <= NT;
   const int my_t = (in_reg && (int)threadIdx.x < P) ? pair_tiles(p, threadIdx.x) : 0;
   int T = 0;
@@ -192,12 +236,12 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
   const int m = ceil_div(wmin, p.tpi_max);
   const int U = ceil_div(wmin, m);
   const bool keep = P <= kPlanPairsLds;
-  const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
   int crun = 0, irun = 0;
   if (keep || publish) {
     for (int b0 = 0; b0 < P; b0 += NT) {
       const int pr = b0 + (int)threadIdx.x;
-      const int t = in_reg ? my_t : (pr < P ? pair_tiles(p, pr) : 0);
+      const int32_t L = pr < P ? pair_len(p, pr) : 0;
+      const int t = in_reg ? my_t : (pr < P ? pair_tiles_of(p, pr, L) : 0);
       int ctot, itot;
       const int cex = crun + block_excl_scan<NT>(pr < P ? pair_cost(t) : 0, scratch, &ctot);
       const int iex = irun + block_excl_scan<NT>(pr < P ? pair_items(cex + kPieceCost, t, U) : 0, scratch, &itot);
@@ -205,6 +249,7 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
         if (keep) {
           cstart[pr] = cex;
           starts[pr] = iex;
+          lens[pr] = L;
         }
         if (publish) p.plan_out[pr] = iex;
       }
@@ -357,13 +402,14 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   __shared__ int tbl[kTableCache];
   __shared__ int starts[kPlanPairsLds + 1];
   __shared__ int cstart[kPlanPairsLds + 1];
+  __shared__ int lens[kPlanPairsLds + 1];
   __shared__ int scratch[16];
 
   const int S = p.S, I = p.I;
   const int bs_mask = (1 << p.bs_log2) - 1;
   const float c = p.c_log2;
 
-  const Plan pl = make_plan(p, starts, cstart, scratch);
+  const Plan pl = make_plan(p, starts, cstart, lens, scratch);
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
 
@@ -410,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int pair = pa.pair;
     const int b = pair / p.shard_count;
     const int s = p.shard_begin + pair % p.shard_count;
-    const int32_t L = checked_len(p.seq_lens, b, p.cap_tokens);
+    const int32_t L = p.pairs <= kPlanPairsLds ? lens[pair] : checked_len(p.seq_lens, b, p.cap_tokens);
     const int n_bs = local_len(L, S, I, s);
     const int nt = tile1 - tile0;
 
