@@ -150,6 +150,16 @@ def test_spike_token_lands_in_its_shard():
         assert np.all(np.argmax(l, axis=0) == (t // I) % S), (t, l[:, 0])
 
 
+def test_many_pairs_take_the_scanning_plan():
+    """More (request, shard) pairs than the plan keeps in LDS (640): the device
+    plan and the item lookup take their scanning paths."""
+    rng = np.random.default_rng(82)
+    lens = [int(x) for x in rng.integers(0, 200, size=90)]
+    lens[3] = 0
+    w = build("many_pairs", lens, R=1, H=16, num_shards=8, interleave=1, seed=82, block_size=16)
+    _check_full(w, "many_pairs")
+
+
 def test_tiny_config():
     _check_full(workloads.tiny(), "tiny_config")
 
