@@ -384,6 +384,15 @@ __device__ __forceinline__ void mfma_vgpr_next(f32x16& s, const bf16x8& a, const
 }
 __device__ __forceinline__ void mfma_vgpr_done(f32x16& s) { asm volatile("s_nop 11" : "+v"(s)); }
 
+// 16 bytes per lane stored with system-scope coherence (sc0 sc1): written
+// through to memory rather than left dirty in this XCD's L2, so the end of
+// the kernel has less to write back before the combine may start.  Used for
+// the whole 1 KiB partial rows; the scattered pieces of fp32 rows are far
+// slower this way and keep ordinary stores.
+__device__ __forceinline__ void store_through(void* ptr, const f32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(ptr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -834,7 +843,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
 #pragma unroll 4
       for (int r = 0; r < kRowsPerWave; ++r) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride + 16 * lane);
-        if ((half_rows >> r) & 1) *reinterpret_cast<f32x4*>(po + (size_t)r * (2 * kVDim)) = v;
+        if ((half_rows >> r) & 1) store_through(po + (size_t)r * (2 * kVDim), v);
       }
     }
   }
