@@ -70,7 +70,7 @@ struct DecodeParams {
   void* part_o;              // [items_cap, rows_total] slots of 512 fp32 (or 512 fp16 in the first half)
   float* part_lse;           // [items_cap, rows_total]
   uint8_t* part_fmt;         // [items_cap, rows_total]: 1 = the slot holds fp16
-  int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, tiles per item
+  int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, cell size U
   int32_t B, R, H, rows_total, row_groups;
   int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
   int32_t S, I, shard_begin, shard_count, pairs;
@@ -907,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float red[8];
 
   const int tid = threadIdx.x;
-  const int quarter = blockIdx.x % (kVDim / C);  // which C-column part
+  const int part_id = blockIdx.x % (kVDim / C);  // which C-column part
   int unit = blockIdx.x / (kVDim / C);
   const int row = unit % p.rows;
   unit /= p.rows;
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
   // pass 2: weighted sum of this block's 128 columns; thread = (source group, 8 columns)
   const int sg = tid / kThreadsPerGroup;
-  const int col = quarter * kCombineCols + 8 * (tid % kThreadsPerGroup);
+  const int col = part_id * kCombineCols + 8 * (tid % kThreadsPerGroup);
   f32x4 acc0 = f32x4{}, acc1 = f32x4{};
   if (!bad && !empty) {
 #pragma unroll 4
@@ -1012,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     f32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = bad ? qnan : (empty ? 0.f : t[e] * inv);
-    const int c0 = quarter * kCombineCols + 4 * tid;
+    const int c0 = part_id * kCombineCols + 4 * tid;
     if (p.mode == kMergeShard) {
       float* out = reinterpret_cast<float*>(p.out) + ((size_t)s_out * p.B * p.rows + orow) * kVDim + c0;
       *reinterpret_cast<f32x4*>(out) = o;
@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       *reinterpret_cast<bf16x4*>(out) = ob;
     }
   }
-  if (quarter != 0) return;
+  if (part_id != 0) return;
 
   const float lse_all = bad ? qnan : (empty ? -INFINITY : m + __builtin_amdgcn_logf(wsum) * kLn2);
   if (p.mode == kMergeShard) {
