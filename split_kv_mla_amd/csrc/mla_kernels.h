@@ -4,28 +4,34 @@
 // Partial kernel (persistent: one workgroup per compute unit, 4 wavefronts,
 // each unit of work = one work item x one group of 128 query rows):
 //   * every workgroup derives the same work plan from seq_lens on the device:
-//     each (request, shard) pair's local tokens are cut into 32-token tiles and
-//     the tiles into items of equal length;
+//     the (request, shard) pairs lie end to end on a cost axis (their
+//     32-token tiles plus a fixed charge per item), cut into equal ranges, one
+//     per workgroup slot; an item is one pair's tiles inside one cell of the
+//     range, so every slot carries the same cost;
 //   * KV tiles (32 tokens x 576 bf16 = 36 KiB) stream HBM -> LDS with 16-byte
-//     direct-to-LDS loads through a 4-deep ring, so three tiles are in flight
-//     while one is consumed; the whole tile is shared by the four wavefronts;
+//     direct-to-LDS loads through a 4-deep ring; the whole tile is shared by
+//     the four wavefronts;
 //   * S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 32x32x16 with fp32
 //     accumulation; P enters as a bf16 pair P_hi + P_lo (two MFMAs on the
-//     same V fragment) so the weights keep ~16 bits.  K rows come from LDS with ds_read_b128, V columns with the
-//     transposing ds_read_b64_tr_b16, Q lives in VGPRs, the 32x512 accumulator
-//     of a wavefront in (A)VGPRs.  V is the first 512 columns of the same
-//     tile: it is never loaded twice;
+//     same V fragment) so the weights keep ~16 bits.  K rows come from LDS
+//     with ds_read_b128, V columns with the transposing ds_read_b64_tr_b16, Q
+//     lives in VGPRs, the 32x512 PV accumulator of a wavefront in AGPRs and
+//     the score accumulator in VGPRs.  V is the first 512 columns of the same
+//     tile: it is never loaded twice.  The walk is pipelined: tile k+1's score
+//     products alternate with tile k's PV products, and its P is formed under
+//     the last of them;
 //   * softmax in fp32 on base-2 scores against a fixed reference: each row's
 //     maximum over the item's first tile (every row with a token in the item
 //     has one there).  Nothing is ever rescaled; if a later score exceeds the
 //     reference by so much that the fp32 denominator passes 2^96, the item is
 //     walked again, first for the exact row maximum, then against it;
-//   * each item writes a normalised partial output and its natural-log LSE;
-//     an item that holds no token of a row writes LSE = -inf and no output.
-// Combine kernel: one workgroup per (request, row, 128-wide slice of the 512
-// output columns) merges the item partials with weights
-// exp2((lse_i - max lse) * log2 e), skipping -inf sources, and writes the
-// bf16 output, the per-shard LSEs and the merged LSE.
+//   * each item writes a normalised partial output (fp16 when the row's
+//     largest |o| is at most 2, else fp32) and its natural-log LSE; an item
+//     that holds no token of a row writes LSE = -inf and no output.
+// Combine kernel: one workgroup per (request, row, C-wide part of the 512
+// output columns; C follows the number of sources) merges the item partials
+// with weights exp2((lse_i - max lse) * log2 e), skipping -inf sources, and
+// writes the bf16 output, the per-shard LSEs and the merged LSE.
 //
 // The method: vLLM PR 50484 ("[Kimi-K3] DCP support") page, "Summary", and its
 // prhub.com.cn summary, "implementation breakdown" step 4 (partial output +
