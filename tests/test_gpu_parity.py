@@ -74,13 +74,48 @@ SMALL = [
     ("h24_rows_not_multiple", [90], 1, 24, 3, 1, 8),
     ("bs1", [50], 1, 16, 2, 1, 1),
     ("rows_512", [200], 4, 128, 2, 1, 64),
+    ("rows_1024_max", [150, 40], 8, 128, 4, 1, 64),
+    ("bs1024_i5", [2500], 1, 32, 3, 5, 1024),
 ]
+
+
+def _sweep(n=12, seed=2026):
+    """Seeded mixed shapes: every row count up to 8, heads not a multiple of
+    32, 1-8 shards, interleaves 1/2/3/16, block sizes 8-256, empty requests,
+    causal and not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        R = int(rng.choice([1, 2, 3, 4, 8]))
+        H = int(rng.choice([8, 16, 40, 64, 100, 128]))
+        while R * H > 1024:
+            H //= 2
+        S = int(rng.integers(1, 9))
+        I = int(rng.choice([1, 2, 3, 16]))
+        bs = int(rng.choice([8, 16, 64, 128, 256]))
+        lens = [int(x) for x in rng.integers(0, 1500, size=int(rng.integers(1, 5)))]
+        if k % 4 == 3:
+            lens.append(0)  # a padding request
+        causal = bool(rng.integers(0, 2))
+        cases.append((f"sweep{k}", lens, R, H, S, I, bs, causal))
+    return cases
+
+
+SWEEP = _sweep()
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_parity(case):
     name, lens, R, H, S, I, bs = case
     w = build(name, lens, R=R, H=H, num_shards=S, interleave=I, seed=zlib.crc32(name.encode()) % 1000, block_size=bs)
+    _check_full(w, name)
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep_parity(case):
+    name, lens, R, H, S, I, bs, causal = case
+    w = build(name, lens, R=R, H=H, num_shards=S, interleave=I, seed=zlib.crc32(name.encode()) % 1000,
+              block_size=bs, causal=causal)
     _check_full(w, name)
 
 
