@@ -10,7 +10,9 @@
 //     range, so every slot carries the same cost;
 //   * KV tiles (32 tokens x 576 bf16 = 36 KiB) stream HBM -> LDS with 16-byte
 //     direct-to-LDS loads through a 4-deep ring; the whole tile is shared by
-//     the four wavefronts;
+//     the four wavefronts; with a single request the query rows are copied
+//     into the idle ring before the plan is formed, so the first item's
+//     start-up does not wait for them;
 //   * S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 32x32x16 with fp32
 //     accumulation; P enters as a bf16 pair P_hi + P_lo (two MFMAs on the
 //     same V fragment) so the weights keep ~16 bits.  K rows come from LDS
@@ -424,9 +426,33 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const int bs_mask = (1 << p.bs_log2) - 1;
   const float c = p.c_log2;
 
-  const Plan pl = make_plan(p, starts, cstart, lens, scratch);
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
+
+  // One request (B = 1): every unit of this workgroup multiplies the same
+  // query rows, so they are copied into the still idle ring before the plan is
+  // formed, and the first unit takes them from there.  Wavefront w copies its
+  // 32 rows into stage w as [64-column group][row][16-byte piece], the piece
+  // slot XOR-keyed by row % 8: each load covers 8 whole 128-byte lines (a
+  // register load in the operand layout touches 32 lines), and the operand
+  // reads below hit 8 distinct bank quads per 8 lanes.
+  bool q_in_ring = false;
+  if (p.B == 1 && (int)(blockIdx.x >> 3) < G * (32 / G)) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup + wave * kRowsPerWave;
+    const uint32_t dst = lds_ring + (uint32_t)(wave * kTileBytes);
+#pragma unroll 4
+    for (int a = 0; a < 36; ++a) {
+      const int r = 8 * (a & 3) + (lane >> 3);  // row within the wavefront
+      const int piece = 8 * (a >> 2) + ((lane & 7) ^ (r & 7));
+      const int qrow = row0 + r < p.rows_total ? row0 + r : 0;  // rows past the end: row 0, never written
+      dma16(p.q + (size_t)qrow * kHeadDim + 8 * piece, dst + 1024u * (uint32_t)a);
+    }
+    q_in_ring = true;
+  }
+
+  const Plan pl = make_plan(p, starts, cstart, lens, scratch);
 
   // Workgroup -> (slot, row group): the row groups of slot j run on XCD j % 8
   // (workgroup i runs on XCD i % 8), walking the same KV tiles at the same
@@ -502,7 +528,22 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       }
     }
     bf16x8 qf[36];
-    {
+    const bool q_from_ring = q_in_ring;
+    q_in_ring = false;
+    if (q_from_ring) {
+      wait_vmcnt<0>();  // the window and (older) the query rows have landed
+      __syncthreads();
+      const char* qs = ring + wave * kTileBytes;
+#pragma unroll
+      for (int db = 0; db < 36; ++db) {
+        const int piece = 2 * db + g;
+        qf[db] = lds_read_b128(qs + 16 * ((((piece >> 3) * kRowsPerWave + l32) << 3) + ((piece & 7) ^ (l32 & 7))));
+      }
+      // in registers before any wavefront passes the barriers below and
+      // loads tiles over these stages
+#pragma unroll
+      for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
+    } else {
       // wave-uniform base (scalar registers) + a per-lane offset
       const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave);
       const uint16_t* qwave = p.q + ((size_t)b * p.rows_total + row0) * kHeadDim;
@@ -512,9 +553,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       const int qlane = (row0 + r_in < p.rows_total ? r_in : -row0) * kHeadDim + 8 * (lane_q >> 5);
 #pragma unroll
       for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qwave + qlane + 16 * db);
+      wait_vmcnt<36>();  // the window has landed (only the 36 Q loads are younger)
+      __syncthreads();
     }
-    wait_vmcnt<36>();  // the window has landed (only the 36 Q loads are younger)
-    __syncthreads();
     bool bad = false;
     for (int i = tid; i < span; i += kThreads) {
       const int v = tbl[i];
@@ -853,6 +894,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       }
     }
   }
+  // a workgroup whose range held no unit still has its query copy in flight
+  if (q_in_ring) wait_vmcnt<0>();
 }
 
 // ------------------------------------------------------------ combine kernel
