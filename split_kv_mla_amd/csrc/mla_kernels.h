@@ -412,6 +412,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Query rows row0 .. row0+31 of request b (one wavefront's rows) copied by
+// LDS-DMA into the ring stage at `dst`, laid out as [64-column group][row]
+// [16-byte piece] with the piece slot XOR-keyed by row % 8: each load covers 8
+// whole 128-byte lines (a register load in the operand layout touches 32), and
+// the operand reads hit 8 distinct bank quads per 8 lanes.  Rows past the end
+// copy row 0 of the request (their outputs are never written).
+__device__ __forceinline__ void copy_q_rows(const DecodeParams& p, int b, int row0, int lane, uint32_t dst) {
+  const uint16_t* qb = p.q + (size_t)b * p.rows_total * kHeadDim;
+#pragma unroll 4
+  for (int a = 0; a < 36; ++a) {
+    const int r = 8 * (a & 3) + (lane >> 3);  // row within the wavefront
+    const int piece = 8 * (a >> 2) + ((lane & 7) ^ (r & 7));
+    const int qrow = row0 + r < p.rows_total ? row0 + r : 0;
+    dma16(qb + (size_t)qrow * kHeadDim + 8 * piece, dst + 1024u * (uint32_t)a);
+  }
+}
+
 // ------------------------------------------------------------ partial kernel
 
 __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
@@ -429,26 +446,15 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
 
-  // One request (B = 1): every unit of this workgroup multiplies the same
-  // query rows, so they are copied into the still idle ring before the plan is
-  // formed, and the first unit takes them from there.  Wavefront w copies its
-  // 32 rows into stage w as [64-column group][row][16-byte piece], the piece
-  // slot XOR-keyed by row % 8: each load covers 8 whole 128-byte lines (a
-  // register load in the operand layout touches 32 lines), and the operand
-  // reads below hit 8 distinct bank quads per 8 lanes.
+  // Every unit reads its query rows from the ring (wavefront w from stage w),
+  // copied there while the ring is idle.  One request (B = 1): every unit of
+  // this workgroup multiplies the same rows, so the first copy is issued
+  // before the plan is formed and overlaps it.
   bool q_in_ring = false;
   if (p.B == 1 && (int)(blockIdx.x >> 3) < G * (32 / G)) {
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row0 = ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup + wave * kRowsPerWave;
-    const uint32_t dst = lds_ring + (uint32_t)(wave * kTileBytes);
-#pragma unroll 4
-    for (int a = 0; a < 36; ++a) {
-      const int r = 8 * (a & 3) + (lane >> 3);  // row within the wavefront
-      const int piece = 8 * (a >> 2) + ((lane & 7) ^ (r & 7));
-      const int qrow = row0 + r < p.rows_total ? row0 + r : 0;  // rows past the end: row 0, never written
-      dma16(p.q + (size_t)qrow * kHeadDim + 8 * piece, dst + 1024u * (uint32_t)a);
-    }
+    copy_q_rows(p, 0, ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup + wave * kRowsPerWave, threadIdx.x & 63,
+                lds_ring + (uint32_t)(wave * kTileBytes));
     q_in_ring = true;
   }
 
@@ -527,34 +533,30 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         if (i < span) dma4(trow + i, __builtin_amdgcn_readfirstlane(tbl_lds + 4u * (uint32_t)(i0 + wave * 64)));
       }
     }
-    bf16x8 qf[36];
-    const bool q_from_ring = q_in_ring;
+    // Q goes through the ring too (behind the window), so the whole prologue is
+    // LDS-DMA with explicit waits: no register load whose wait the compiler
+    // would place (and, not counting the DMA, place too late: after tile 0).
+    if (!q_in_ring)
+      copy_q_rows(p, b, __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave), lane,
+                  lds_ring + (uint32_t)(wave * kTileBytes));
     q_in_ring = false;
-    if (q_from_ring) {
-      wait_vmcnt<0>();  // the window and (older) the query rows have landed
-      __syncthreads();
+    wait_vmcnt<0>();  // the window and the query rows have landed
+    __syncthreads();
+    bf16x8 qf[36];
+    {
+      int lane_q = lane;  // opaque copy: nothing of the read addresses stays live
+      asm volatile("" : "+v"(lane_q));
+      const int r_q = lane_q & 31, g_q = lane_q >> 5;
       const char* qs = ring + wave * kTileBytes;
 #pragma unroll
       for (int db = 0; db < 36; ++db) {
-        const int piece = 2 * db + g;
-        qf[db] = lds_read_b128(qs + 16 * ((((piece >> 3) * kRowsPerWave + l32) << 3) + ((piece & 7) ^ (l32 & 7))));
+        const int piece = 2 * db + g_q;
+        qf[db] = lds_read_b128(qs + 16 * ((((piece >> 3) * kRowsPerWave + r_q) << 3) + ((piece & 7) ^ (r_q & 7))));
       }
       // in registers before any wavefront passes the barriers below and
       // loads tiles over these stages
 #pragma unroll
       for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
-    } else {
-      // wave-uniform base (scalar registers) + a per-lane offset
-      const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerGroup + wave * kRowsPerWave);
-      const uint16_t* qwave = p.q + ((size_t)b * p.rows_total + row0) * kHeadDim;
-      int lane_q = lane;  // opaque copy: recomputing beats spilling the lane terms
-      asm volatile("" : "+v"(lane_q));
-      const int r_in = lane_q & 31;
-      const int qlane = (row0 + r_in < p.rows_total ? r_in : -row0) * kHeadDim + 8 * (lane_q >> 5);
-#pragma unroll
-      for (int db = 0; db < 36; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(qwave + qlane + 16 * db);
-      wait_vmcnt<36>();  // the window has landed (only the 36 Q loads are younger)
-      __syncthreads();
     }
     bool bad = false;
     for (int i = tid; i < span; i += kThreads) {
@@ -589,13 +591,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     };
     auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
-    // Prologue: tile 0; Q (loaded above, behind the table window) and tile 0
-    // must both be resident before the first tile, and waiting for them here
-    // (the compiler waits before the register pin) keeps any wait for Q out of
-    // the tile loop.  Then tiles 1 and 2.
+    // Prologue: tiles 0, 1 and 2 back to back (Q is already in registers).
     issue_tile(tile0, 0);
-#pragma unroll
-    for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
     issue_tile(tile0 + 1, 1);
     issue_tile(tile0 + 2, 2);
 
