@@ -187,8 +187,9 @@ struct Plan {
 // the same cost give or take one cell's rounding.  Cost and item prefixes per
 // pair go to `cstart` / `starts` (LDS) when the pairs fit, and workgroup 0
 // publishes the item prefixes with the item total and U for the combine.
+// len0: with a single request, its length (unchecked), already loaded.
 template <int NT = kThreads>
-__device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* lens, int* scratch) {
+__device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* lens, int* scratch, int32_t len0) {
   const int P = p.pairs;
   const bool publish = (blockIdx.x == 0) && (p.plan_out != nullptr);
   if (P <= 64) {
@@ -196,7 +197,12 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
     // wait at a single barrier
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
-      const int32_t L = lane < P ? pair_len(p, lane) : 0;
+      int32_t L = 0;
+      if (p.B == 1) {  // wave-uniform: no vector load of seq_lens on this path
+        if (lane < P) L = (len0 < 0 || len0 > p.cap_tokens) ? 0 : len0;
+      } else if (lane < P) {
+        L = pair_len(p, lane);
+      }
       const int t = lane < P ? pair_tiles_of(p, lane, L) : 0;
       const int cost = pair_cost(t);
       const int cinc = wave_incl_scan(cost);
@@ -450,6 +456,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   // copied there while the ring is idle.  One request (B = 1): every unit of
   // this workgroup multiplies the same rows, so the first copy is issued
   // before the plan is formed and overlaps it.
+  // One request: its length comes through the scalar cache, issued before the
+  // query copy so that it does not queue behind those vector loads.
+  int32_t len0 = -1;
+  if (p.B == 1) len0 = *(const __attribute__((address_space(4))) int32_t*)(p.seq_lens);
   bool q_in_ring = false;
   if (p.B == 1 && (int)(blockIdx.x >> 3) < G * (32 / G)) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     q_in_ring = true;
   }
 
-  const Plan pl = make_plan(p, starts, cstart, lens, scratch);
+  const Plan pl = make_plan(p, starts, cstart, lens, scratch, len0);
 
   // Workgroup -> (slot, row group): the row groups of slot j run on XCD j % 8
   // (workgroup i runs on XCD i % 8), walking the same KV tiles at the same
