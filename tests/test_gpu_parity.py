@@ -282,6 +282,27 @@ def test_seq_len_beyond_table_is_nan():
     assert np.isfinite(out[0]).all()
 
 
+@pytest.mark.parametrize("bad_len", [8 * 16 + 1, -3], ids=["beyond_table", "negative"])
+def test_single_request_bad_seq_len_is_nan(bad_len):
+    """A single request's length takes the scalar path into the plan; an
+    out-of-range one is still read as empty and reported as NaN."""
+    w = build("badlen1", [100], R=1, H=16, num_shards=2, interleave=1, seed=38, block_size=16, max_blocks=8)
+    w.seq_lens[0] = bad_len
+    _say(f"[parity] single request, seq_len {bad_len}")
+    out, lse, lf = _run_split(w)
+    assert np.isnan(out).all() and np.isnan(lf).all() and np.isnan(lse).all()
+
+
+def test_single_empty_request():
+    """B = 1 with seq_len 0 (a graph-padding step): +0.0 output, -inf LSEs."""
+    w = build("empty1", [16], R=1, H=16, num_shards=2, interleave=1, seed=39, block_size=16)
+    w.seq_lens[0] = 0  # the step's table row still names a block; none of it is read
+    _say("[parity] single request, seq_len 0")
+    out, lse, lf = _run_split(w)
+    assert np.all(out == 0.0) and not np.signbit(out).any()
+    assert np.isneginf(lse).all() and np.isneginf(lf).all()
+
+
 def test_batch_zero_is_noop():
     m = _lib()
     q = torch.empty((0, 1, 16, 576), dtype=torch.bfloat16, device="cuda")
