@@ -189,8 +189,8 @@ def main():
         print(json.dumps(summarize_counters(*args.summarize_counters, name, calib), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the shards are virtual, on one device)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the S shards are virtual, all on one device)", file=sys.stderr)
         sys.exit(2)
     import torch
     import split_kv_mla_amd as mla

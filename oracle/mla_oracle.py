@@ -43,7 +43,7 @@ and partial outputs, the same definition restricted to each shard's token
 set.  ``lse_combine_oracle`` is the textbook LSE-weighted merge, used for the
 standalone combine entry point and for the split-then-merge invariant.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 natural-log LSE; shard of global token t is (t // I) mod S; with ``causal``
 row r of R sees seq_len - (R - 1 - r) tokens (seq_len counts the R new
 tokens), otherwise every row sees seq_len tokens; a row that sees no token

@@ -10,7 +10,7 @@ request (114k shared prefix + 6k suffix, "[Kimi-K3] DCP support" PR 50484
 page, section "Performance"), and 1 + 3 verification rows per request
 ("perf(mla): fuse K3 DCP verification queries" PR 565 page, "Summary").
 
-Conventions (listed in the design doc with the rest of the input recipe):
+Conventions:
 * values: float32 standard normal, rounded to bf16 round-to-nearest-even;
 * physical block 0 is a NaN poison block; unused table entries point at it;
   slots past a request's length in its last block are NaN;
