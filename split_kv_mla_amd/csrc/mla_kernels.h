@@ -424,10 +424,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // whole 128-byte lines (a register load in the operand layout touches 32), and
 // the operand reads hit 8 distinct bank quads per 8 lanes.  Rows past the end
 // copy row 0 of the request (their outputs are never written).
-__device__ __forceinline__ void copy_q_rows(const DecodeParams& p, int b, int row0, int lane, uint32_t dst) {
+// Loads a0 .. a1-1 of the 36 (each 8 rows x 128 bytes).
+__device__ __forceinline__ void copy_q_rows(const DecodeParams& p, int b, int row0, int lane, uint32_t dst,
+                                            int a0 = 0, int a1 = 36) {
   const uint16_t* qb = p.q + (size_t)b * p.rows_total * kHeadDim;
 #pragma unroll 4
-  for (int a = 0; a < 36; ++a) {
+  for (int a = a0; a < a1; ++a) {
     const int r = 8 * (a & 3) + (lane >> 3);  // row within the wavefront
     const int piece = 8 * (a >> 2) + ((lane & 7) ^ (r & 7));
     const int qrow = row0 + r < p.rows_total ? row0 + r : 0;
@@ -452,19 +454,24 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
 
-  // Every unit reads its query rows from the ring (wavefront w from stage w),
-  // copied there while the ring is idle.  One request (B = 1): every unit of
-  // this workgroup multiplies the same rows, so the first copy is issued
-  // before the plan is formed and overlaps it.
   // One request: its length comes through the scalar cache, issued before the
   // query copy so that it does not queue behind those vector loads.
   int32_t len0 = -1;
   if (p.B == 1) len0 = *(const __attribute__((address_space(4))) int32_t*)(p.seq_lens);
+  // Every unit reads its query rows from the ring (wavefront w from stage w),
+  // copied there while the ring is idle.  One request (B = 1): every unit of
+  // this workgroup multiplies the same rows, so the first copy is issued
+  // before the plan is formed and overlaps it.  Wavefront 0 forms the plan:
+  // wavefronts 1-3 copy its rows (a third each) besides their own, so that
+  // it does not wait behind the copy's loads to issue them.
   bool q_in_ring = false;
   if (p.B == 1 && (int)(blockIdx.x >> 3) < G * (32 / G)) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    copy_q_rows(p, 0, ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup + wave * kRowsPerWave, threadIdx.x & 63,
-                lds_ring + (uint32_t)(wave * kTileBytes));
+    const int rg0 = ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup;
+    if (wave != 0) {
+      copy_q_rows(p, 0, rg0 + wave * kRowsPerWave, threadIdx.x & 63, lds_ring + (uint32_t)(wave * kTileBytes));
+      copy_q_rows(p, 0, rg0, threadIdx.x & 63, lds_ring, 12 * (wave - 1), 12 * wave);
+    }
     q_in_ring = true;
   }
 
