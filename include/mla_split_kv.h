@@ -75,7 +75,8 @@ typedef struct mla_decode_args {
   int32_t num_blocks;         /* physical blocks in kv_cache, >= 1                       */
   int32_t block_size;         /* tokens per block: a power of two, 1..1024               */
   int32_t max_blocks_per_seq; /* width of block_table, >= 1                              */
-  int32_t num_shards;         /* S >= 1                                                  */
+  int32_t num_shards;         /* S >= 1; S * I <= 2^24 and B * S <= 2^20 (else          */
+                              /* MLA_ERR_UNSUPPORTED)                                    */
   int32_t interleave;         /* I >= 1: token t -> shard (t / I) % S                    */
   float softmax_scale;        /* multiplies q.k before the softmax, e.g. 1/sqrt(192)     */
   int32_t causal;             /* nonzero: verification rows see a causal tail            */
