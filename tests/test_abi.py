@@ -162,6 +162,11 @@ def test_bad_arguments_return_errors_without_launching():
                                 ctypes.c_void_p(8), 1 << 40, null) == -2
     # combine with bad sizes
     assert lib.mla_lse_combine(null, null, 0, 1, 1, 16, null, null, null) == -1
+    # shard geometry beyond what the kernels' 32-bit shard arithmetic covers
+    c = _args(S=4097, I=4096)  # S * I > 2^24
+    assert lib.mla_workspace_bytes(ctypes.byref(c)) == 0
+    assert lib.mla_split_decode(ctypes.byref(c), ctypes.c_void_p(8), ctypes.c_void_p(8), null,
+                                ctypes.c_void_p(8), 1 << 40, null) == -2
 
 
 def test_batch_zero_returns_ok_without_launching():
