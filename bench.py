@@ -10,7 +10,9 @@ replayed between two device synchronisations; ms_per_step is that wall time
 divided by K.  The K steps cycle through several copies of the KV cache whose
 total exceeds the 256 MB Infinity Cache, so KV bytes come from HBM.  The
 partial kernel's own duration is measured live with HIP events recorded by the
-library on its stream (eager steps), and gives the roofline fraction.
+library on its stream (eager steps), and gives the roofline fraction;
+partial_kernel_ms_warm is the same kernel fed the same KV copy every step
+(held in the Infinity Cache when it fits), reported beside it.
 
 roofline.traffic comes from a committed counter summary
 (profiles/<kernel>_<workload>_counters.json, written by --summarize-counters
@@ -52,8 +54,9 @@ def parse():
                     choices=["long", "long_b2", "batch", "verify", "padded", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-one-shard", action="store_true",
-                    help="skip the one-shard partial launches (profiled runs, so that every "
-                         "partial-kernel dispatch is a full step's)")
+                    help="skip the one-shard and the warm (same KV copy) partial launches "
+                         "(profiled runs, so that every partial-kernel dispatch is a full, "
+                         "HBM-fed step's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -158,9 +161,30 @@ def kernel_bytes(w):
     return w.unique_kv_tokens * ROW_BYTES + w.B * w.R * w.H * ROW_BYTES
 
 
+def host_description():
+    """CPU model and the BLAS numpy links against, for the CPU baseline's record."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown BLAS"
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg["Build Dependencies"]["blas"]["name"]
+    except Exception:
+        pass
+    return model, blas
+
+
 def cpu_baseline(w, budget_s):
     import oracle
     threads = len(os.sched_getaffinity(0))
+    model, blas = host_description()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
@@ -172,7 +196,7 @@ def cpu_baseline(w, budget_s):
     tokens = reps * int(w.seq_lens.astype(np.int64).sum())
     return {"value": tokens / el, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full run(s) of the float64 oracle (unsplit + per-shard attention) "
-                      f"on this workload, {el:.1f} s, numpy BLAS threads = {threads}"}
+                      f"on this workload, {el:.1f} s, numpy BLAS ({blas}) threads = {threads}, {model}"}
 
 
 def pct(xs, q):
@@ -248,6 +272,20 @@ def main():
         part_ms.append(e[0].elapsed_time(e[1]))
         comb_ms.append(e[1].elapsed_time(e[2]))
 
+    # warm: the same KV copy every step, so it sits in the 256 MB Infinity
+    # Cache when it fits (reported beside the cycled, HBM-fed figures)
+    warm_ms = []
+    for i in range(0 if args.no_one_shard else args.event_steps + 2):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for x in e:
+            x.record()
+        torch.cuda.synchronize()
+        mla.mla_split_decode(q, kvs[0], bt, sl, S, I, w.scale, w.causal, out=out, lse=lse, lse_final=lf,
+                             workspace=ws, events=e)
+        torch.cuda.synchronize()
+        if i >= 2:
+            warm_ms.append(e[0].elapsed_time(e[1]))
+
     # one DCP rank's share: the partial kernel over shard 0 alone
     rank_ms = []
     n_one_shard = 0 if args.no_one_shard else args.event_steps + 2
@@ -312,6 +350,7 @@ def main():
         "partial_kernel_ms_p10_p50_p90": [pct(part_ms, 0.1), pct(part_ms, 0.5), pct(part_ms, 0.9)],
         "combine_kernel_ms": statistics.mean(comb_ms),
         "combine_kernel_ms_p10_p50_p90": [pct(comb_ms, 0.1), pct(comb_ms, 0.5), pct(comb_ms, 0.9)],
+        "partial_kernel_ms_warm": statistics.median(warm_ms) if warm_ms else None,
         "one_shard_partial_ms": statistics.median(rank_ms) if rank_ms else None,
         "mfma_tflops_partial": flops / (part_avg / 1e3) / 1e12,
         "mfma_frac_of_bf16_peak": flops / (part_avg / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
