@@ -69,8 +69,11 @@ inline int32_t max_tiles_per_item(int32_t S, int32_t I, int32_t block_size) {
 
 // Cost, in tiles' worth of time, of one more item: the prologue that loads
 // its block-table window, q and first tiles, and the epilogue that writes
-// its partial.  The even split charges it once per (request, shard) pair.
-constexpr int kPieceCost = 8;
+// its partial (128 rows of 1 KiB whatever the item's length).  The even
+// split charges it once per (request, shard) pair.  Measured: a workgroup of
+// twelve 1-tile items takes as long as ~11 tiles per item; of the charges
+// tried on the padded batch (8, 10, 11, 12, 14) 11 balances it best.
+constexpr int kPieceCost = 11;
 
 // Cost units of a pair with `tiles` tiles (a pair without tokens costs nothing).
 MLA_HD int32_t pair_cost(int32_t tiles) { return tiles > 0 ? tiles + kPieceCost : 0; }

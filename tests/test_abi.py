@@ -61,7 +61,14 @@ def test_workspace_sizing():
         assert m.mla_workspace_bytes(_args(**bad)) == 0, bad
 
 
-PIECE_COST = 8  # kPieceCost of the device plan
+def _piece_cost():
+    """kPieceCost of the device plan, read from its header."""
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "split_kv_mla_amd", "csrc", "mla_plan.h")).read()
+    return int(re.search(r"constexpr int kPieceCost = (\d+);", src).group(1))
+
+
+PIECE_COST = _piece_cost()
 
 
 def _tpi_max(S, I, bs):
