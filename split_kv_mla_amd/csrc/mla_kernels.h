@@ -868,26 +868,51 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
     const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
     if (live && g == 0) p.part_fmt[prow] = as_half ? 1 : 0;
-    // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3]
-    if (live && !as_half) {
-      float* po = reinterpret_cast<float*>(p.part_o) + prow * kVDim + 4 * g;
+    // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3].
+    // Rows leave through the idle ring, transposed so that a store writes a
+    // whole 1 KiB piece of a row (the scattered pieces of the register layout
+    // would cost a write request each).  Each wavefront uses its own region
+    // (32 rows of 1040 bytes), so only its own LDS order matters.
+    constexpr int kStride = 2 * kVDim + 16;    // bytes per staged fp16 row (16 of padding)
+    constexpr int kStride32 = 4 * kVDim + 16;  // bytes per staged fp32 row
+    static_assert(16 * kStride32 <= kRowsPerWave * kStride, "fp32 half of the rows fits the region");
+    char* stage = ring + wave * (kRowsPerWave * kStride);
+    const size_t prow0 = (size_t)item * p.rows_total + rg * kRowsPerGroup + wave * kRowsPerWave;
+    // fp32 rows: 16 rows of the wavefront at a time, each row two 1 KiB stores
+    const uint64_t f32_rows = __ballot(live && !as_half && g == 0);  // bit r: row l32 = r
+    if (f32_rows) {
+      float* po = reinterpret_cast<float*>(p.part_o) + prow0 * kVDim + 4 * lane;
 #pragma unroll
-      for (int db = 0; db < 16; ++db)
+      for (int half = 0; half < 2; ++half) {
+        if ((f32_rows >> (16 * half)) & 0xffffu) {
+          if ((l32 >> 4) == half) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
+            for (int db = 0; db < 16; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q) = v;
+              for (int q = 0; q < 4; ++q) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
+                *reinterpret_cast<f32x4*>(stage + (l32 & 15) * kStride32 + 4 * (32 * db + 8 * q + 4 * g)) = v;
+              }
+          }
+          asm volatile("" ::: "memory");  // the reads below see every lane's writes
+#pragma unroll 2
+          for (int r = 0; r < 16; ++r) {
+            if ((f32_rows >> (16 * half + r)) & 1) {
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride32 + 1024 * c + 16 * lane);
+                store_through(po + (size_t)(16 * half + r) * kVDim + 256 * c, v);
+              }
+            }
+          }
+          asm volatile("" ::: "memory");  // read before the next half overwrites the region
         }
+      }
     }
-    // fp16 rows leave through the idle ring, transposed so that one store
-    // writes a whole 1 KiB row (the scattered 8-byte pieces of the register
-    // layout would cost a write request each).  Each wavefront uses its own
-    // region (32 rows of 1040 bytes), so only its own LDS order matters.
+    // fp16 rows: the whole wavefront's 32 rows at once
     {
-      constexpr int kStride = 2 * kVDim + 16;  // bytes per staged row (16 of padding)
-      char* stage = ring + wave * (kRowsPerWave * kStride);
 #pragma unroll
       for (int db = 0; db < 16; ++db)
 #pragma unroll
@@ -899,7 +924,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         }
       asm volatile("" ::: "memory");  // the reads below see every lane's writes
       const uint64_t half_rows = __ballot(as_half && g == 0);  // bit r: row l32 = r
-      const size_t prow0 = (size_t)item * p.rows_total + rg * kRowsPerGroup + wave * kRowsPerWave;
       _Float16* po = reinterpret_cast<_Float16*>(p.part_o) + prow0 * (2 * kVDim) + 8 * lane;
 #pragma unroll 4
       for (int r = 0; r < kRowsPerWave; ++r) {
