@@ -9,7 +9,8 @@
 //     per workgroup slot; an item is one pair's tiles inside one cell of the
 //     range, so every slot carries the same cost;
 //   * KV tiles (32 tokens x 576 bf16 = 36 KiB) stream HBM -> LDS with 16-byte
-//     direct-to-LDS loads through a 4-deep ring; the whole tile is shared by
+//     direct-to-LDS loads through a 4-stage ring (the walk keeps two tiles in
+//     flight ahead of the one it consumes); the whole tile is shared by
 //     the four wavefronts; with a single request the query rows are copied
 //     into the idle ring before the plan is formed, so the first item's
 //     start-up does not wait for them;
@@ -62,6 +63,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTileBytes = kTile * kHeadDim * 2;  // 36864
 constexpr int kStages = 4;                        // LDS ring depth (147456 bytes)
+constexpr int kLead = 2;                          // tiles in flight ahead of the walk (<= kStages - 1)
 constexpr int kRowsPerGroup = 4 * kRowsPerWave;   // 128 query rows per workgroup
 constexpr int kNumCUs = 256;                      // MI355X compute units: the persistent grid
 constexpr int kPlanPairsLds = 640;                // per-pair plan prefixes and lengths kept in LDS
@@ -608,10 +610,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     };
     auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
-    // Prologue: tiles 0, 1 and 2 back to back (Q is already in registers).
-    issue_tile(tile0, 0);
-    issue_tile(tile0 + 1, 1);
-    issue_tile(tile0 + 2, 2);
+    // Prologue: the walk's first kLead tiles back to back (Q is already in
+    // registers).
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) issue_tile(tile0 + k, k);
 
     f32x16 acc[16];
     float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
@@ -670,9 +672,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
 
+      // tiles kept in flight ahead of the tile being consumed
+      constexpr int kAheadTiles = kMaxOnly ? kStages - 1 : kLead;
       if (!prologue_issued)
-        for (int k = 0; k < kStages - 1; ++k) issue_tile(tile0 + k, k);
-      const char* next_src = tile_src(tile0 + kStages - 1);
+        for (int k = 0; k < kAheadTiles; ++k) issue_tile(tile0 + k, k);
+      const char* next_src = tile_src(tile0 + kAheadTiles);
       float m_walk = -INFINITY;
 
       // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4)):
@@ -744,7 +748,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           if (younger >= 2) wait_vmcnt<18>();
           else if (younger == 1) wait_vmcnt<9>();
           else wait_vmcnt<0>();
-          // every wavefront is past tile k-1: its stage takes tile k+3
+          // every wavefront is past tile k-1: its stage takes tile k+3 (this
+          // slow-path walk keeps kStages - 1 tiles in flight)
           lds_barrier();
           if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
           next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
@@ -757,7 +762,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         // scores in the VGPR chain while tile k's PV products run on the AGPR
         // accumulator, and tile k+1's P under the last of those products, so
         // the matrix pipe does not wait for the softmax.
-        wait_vmcnt<18>();  // tile 0 (tiles 1 and 2 in flight)
+        static_assert(kLead == 2 || kLead == 3, "DMA waits below");
+        if constexpr (kLead == 3) wait_vmcnt<18>();  // tile 0 (tiles 1 and 2 in flight)
+        else wait_vmcnt<9>();                        // tile 0 (tile 1 in flight)
         lds_barrier();
         PFrag pf;
         {
@@ -770,16 +777,16 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           const bool more = k + 1 < nt;
           if (more) {
             // tile k+1 resident: the loads issued so far are the prologue's
-            // three plus one per earlier iteration that still had a tile to load
-            const int younger = 3 + max(0, min(k, nt - kStages + 1)) - (k + 2);
+            // kLead plus one per earlier iteration that still had a tile to load
+            const int younger = kLead + max(0, min(k, nt - kLead)) - (k + 2);
             if (younger >= 1) wait_vmcnt<9>();
             else wait_vmcnt<0>();
           }
-          // every wavefront is past iteration k-1 (tile k-1's products): its
-          // stage takes tile k+3
+          // every wavefront is past iteration k-1 (tile k-1's products): the
+          // stage of tile k + kLead - kStages takes tile k + kLead
           lds_barrier();
-          if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
-          next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
+          if (k + kLead < nt) issue_src(next_src, (k + kLead) % kStages);
+          next_src = tile_src(tile0 + k + kLead + 1);  // clamped past the end: harmless
           const char* buf = ring + (k % kStages) * kTileBytes;
           const char* nbuf = ring + ((k + 1) % kStages) * kTileBytes;
           // O^T[dim][row] += V^T[dim][token] P^T[token][row]: product i uses
