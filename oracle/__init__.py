@@ -19,5 +19,6 @@ from .mla_oracle import (  # noqa: F401
     attention_row,
     mla_decode_oracle,
     lse_combine_oracle,
+    merge_states_oracle,
     padding_row_mask,
 )

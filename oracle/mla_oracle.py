@@ -31,6 +31,13 @@ What is computed, and where the pages define it
   ``mask_dcp_empty_shards_``.
 * The LSE is float32 in the product (PR 50484 page, "CUDA-graph padding
   follow-up": return-LSE dtype assertions saw float32 values).
+* Two-way merge of attention states (a prefix and a suffix, the chunked-
+  context use of the same LSE merge), which the product computes safely in
+  place: its output may be the prefix's own buffers.  Source: "perf(mla):
+  fuse K3 DCP verification queries" PR 565 page, the commit text on caching
+  each head's prefix and suffix LSEs before any output write, reading the
+  LSEs through their declared strides, and the six-head, 128-element
+  coverage at 256 and 4096 tokens.
 * Verification rows: a request contributes R query rows (1 + K drafts) that
   all read that request's KV ("perf(mla): fuse K3 DCP verification queries",
   PR 565 page, "Summary"); per-row lengths are formed after expanding
@@ -196,6 +203,41 @@ def lse_combine_oracle(out_partial, lse):
         out[idx] = acc / w.sum()
         lse_out[idx] = M + math.log(w.sum())
     return out, lse_out
+
+
+def merge_states_oracle(prefix, prefix_lse, suffix, suffix_lse):
+    """Merge of two attention states over disjoint key sets, by their LSEs.
+
+    prefix, suffix [T, H, D]; prefix_lse, suffix_lse [H, T] (natural log).
+    Per (t, h) with M = max of the two LSEs and a = exp(lse_prefix - M),
+    b = exp(lse_suffix - M): out = (a * prefix + b * suffix) / (a + b) and
+    lse = M + ln(a + b).  A side whose LSE is -inf has weight zero and its
+    payload is never read; when both are -inf, out = +0.0 and lse = -inf.
+    PR 565 page, commit text on the prefix/suffix LSE merge.
+    """
+    prefix = np.asarray(prefix, dtype=np.float64)
+    suffix = np.asarray(suffix, dtype=np.float64)
+    lp = np.asarray(prefix_lse, dtype=np.float64)
+    ls = np.asarray(suffix_lse, dtype=np.float64)
+    T, H, D = prefix.shape
+    out = np.zeros((T, H, D))
+    lse = np.full((H, T), -np.inf)
+    for t in range(T):
+        for h in range(H):
+            a_lse, b_lse = lp[h, t], ls[h, t]
+            if a_lse == -np.inf and b_lse == -np.inf:
+                continue
+            M = max(a_lse, b_lse)
+            a = 0.0 if a_lse == -np.inf else math.exp(a_lse - M)
+            b = 0.0 if b_lse == -np.inf else math.exp(b_lse - M)
+            acc = np.zeros(D)
+            if a > 0.0:
+                acc += a * prefix[t, h]
+            if b > 0.0:
+                acc += b * suffix[t, h]
+            out[t, h] = acc / (a + b)
+            lse[h, t] = M + math.log(a + b)
+    return out, lse
 
 
 def padding_row_mask(seq_lens, query_start_loc):

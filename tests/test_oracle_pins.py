@@ -333,3 +333,52 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
         except AssertionError:
             caught = True
     assert caught, mutation
+
+
+# --- two-way prefix/suffix merge -------------------------------------------
+
+def _split_attention_states(T, H, n_prefix, n_suffix, seed):
+    """Attention of T x H queries over a prefix and a suffix key set, each on
+    its own, and over their union: [T, H, D] outputs with [H, T] LSEs."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, mla_oracle.D_QK))
+    K = rng.standard_normal((n_prefix + n_suffix, mla_oracle.D_QK))
+    scale = 1 / math.sqrt(192)
+    op, lp = mla_oracle.attention_row(q, K[:n_prefix], scale)
+    os_, ls = mla_oracle.attention_row(q, K[n_prefix:], scale)
+    ou, lu = mla_oracle.attention_row(q, K, scale)
+    return (op, lp.T, os_, ls.T), (ou, lu.T)
+
+
+@pytest.mark.parametrize("n_prefix,n_suffix", [(1, 1), (7, 40), (300, 3)])
+def test_merge_states_equals_attention_over_the_union(n_prefix, n_suffix):
+    """Softmax over a disjoint union, written as a merge of its two parts."""
+    (op, lp, os_, ls), (ou, lu) = _split_attention_states(3, 6, n_prefix, n_suffix, seed=n_prefix)
+    out, lse = oracle.merge_states_oracle(op, lp, os_, ls)
+    np.testing.assert_allclose(out, ou, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lu, rtol=0, atol=1e-12)
+    # the merge is symmetric in its two sides
+    out2, lse2 = oracle.merge_states_oracle(os_, ls, op, lp)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+
+
+def test_merge_states_empty_side_returns_the_other():
+    """A side with LSE -inf (no keys) has weight zero and is never read."""
+    (op, lp, os_, ls), _ = _split_attention_states(2, 4, 5, 9, seed=11)
+    lp = lp.copy()
+    lp[1, 0] = -np.inf
+    op = op.copy()
+    op[0, 1] = np.nan
+    out, lse = oracle.merge_states_oracle(op, lp, os_, ls)
+    assert np.array_equal(out[0, 1], os_[0, 1]) and lse[1, 0] == ls[1, 0]
+    both = np.full_like(lp, -np.inf)
+    out, lse = oracle.merge_states_oracle(np.full_like(op, np.nan), both, np.full_like(os_, np.nan), both)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_merge_states_closed_form_equal_lse():
+    """Equal LSEs: the plain average, and the LSE grows by ln 2."""
+    p, s = np.full((1, 1, 128), 3.0), np.full((1, 1, 128), -1.0)
+    out, lse = oracle.merge_states_oracle(p, np.array([[0.5]]), s, np.array([[0.5]]))
+    assert np.all(out == 1.0) and lse[0, 0] == pytest.approx(0.5 + math.log(2.0), abs=1e-15)
