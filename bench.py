@@ -57,6 +57,8 @@ def parse():
                     help="skip the one-shard and the warm (same KV copy) partial launches "
                          "(profiled runs, so that every partial-kernel dispatch is a full, "
                          "HBM-fed step's)")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the timing of the two-way prefix/suffix merge")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -199,6 +201,37 @@ def cpu_baseline(w, budget_s):
                       f"on this workload, {el:.1f} s, numpy BLAS ({blas}) threads = {threads}, {model}"}
 
 
+MERGE_T, MERGE_H, MERGE_D = 131072, 6, 128
+
+
+def merge_leg(mla, dev, launches):
+    """Time the two-way merge in place (out = prefix) on T x 6 heads x 128 bf16
+    states: per launch it reads both states and LSEs and writes one state and
+    one LSE."""
+    import torch
+    gen = torch.Generator(device=dev).manual_seed(7)
+    shape = (MERGE_T, MERGE_H, MERGE_D)
+    p = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    s = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    lp = torch.rand((MERGE_H, MERGE_T), generator=gen, device=dev) * 15 - 3
+    ls = torch.rand((MERGE_H, MERGE_T), generator=gen, device=dev) * 15 - 3
+    ms = []
+    for i in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mla.mla_merge_states(p, lp, s, ls, out=p, out_lse=lp)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    rows = MERGE_T * MERGE_H
+    nbytes = 3 * rows * MERGE_D * 2 + 3 * rows * 4
+    med = statistics.median(ms)
+    gbps = nbytes / (med / 1e3) / 1e9
+    return {"kernel": "mla::merge_kernel<1>", "workload": f"T={MERGE_T} H={MERGE_H} D={MERGE_D} bf16, in place",
+            "ms": med, "bytes_per_launch": nbytes, "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+
+
 def pct(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
@@ -301,6 +334,9 @@ def main():
         if i >= 2:
             rank_ms.append(e0.elapsed_time(e1))
 
+    # the two-way prefix/suffix merge, in place, on a chunked-context shape
+    merge = None if args.no_merge else merge_leg(mla, dev, args.event_steps + 2)
+
     # K steps in one graph, replayed between synchronisations
     K = args.steps
     g = torch.cuda.CUDAGraph()
@@ -359,6 +395,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(w.name),
                      "kernel": PARTIAL_KERNEL, "bytes_per_launch": kb},
     }
+    if merge is not None:
+        rec["merge_states"] = merge
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

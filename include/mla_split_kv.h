@@ -110,6 +110,32 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
 int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
                     int32_t rows, int32_t heads, void* out, float* lse_final, void* stream);
 
+/* Two-way merge of attention states over disjoint key sets (a prefix and a
+ * suffix), the chunked-context use of the LSE merge ("perf(mla): fuse K3 DCP
+ * verification queries", PR 565 page, commit text on the prefix/suffix merge
+ * and its in-place use):
+ *   prefix, suffix  [tokens, heads, head_dim] of `dtype` (0 float32,
+ *                   1 bf16, 2 fp16), rows contiguous, 16-byte aligned;
+ *   *_lse           float32, element (h, t) at lse[h * stride_head +
+ *                   t * stride_token] (strides in elements, >= 0);
+ *   out             [tokens, heads, head_dim] of `dtype`:
+ *                   (a * prefix + b * suffix) / (a + b) per row, with
+ *                   a = exp(lse_p - M), b = exp(lse_s - M), M = max(lse_p, lse_s);
+ *                   a side whose LSE is -inf is never read; +0.0 where both are;
+ *   out_lse         float32 or NULL: M + ln(a + b), -inf where both are -inf.
+ * In place: out may be exactly prefix or suffix, and out_lse exactly
+ * prefix_lse or suffix_lse with the same strides; any other overlap between
+ * an output and an input is rejected (MLA_ERR_INVALID_ARG), as are
+ * misaligned pointers, negative strides, or dtype outside 0..2.  head_dim *
+ * element size must be a multiple of 16 bytes and at most 64 KiB
+ * (MLA_ERR_UNSUPPORTED).  out_lse's strides must give every row its own slot.
+ * LSEs are expected finite or -inf.  tokens == 0 enqueues nothing. */
+int mla_merge_states(void* out, float* out_lse, int64_t out_lse_stride_head, int64_t out_lse_stride_token,
+                     const void* prefix, const float* prefix_lse, int64_t prefix_lse_stride_head,
+                     int64_t prefix_lse_stride_token, const void* suffix, const float* suffix_lse,
+                     int64_t suffix_lse_stride_head, int64_t suffix_lse_stride_token, int32_t tokens,
+                     int32_t heads, int32_t head_dim, int32_t dtype, void* stream);
+
 /* The whole path: partial attention of every shard, then the LSE combine.
  *   out        bf16 [B, R, H, 512]: attention over each row's whole KV;
  *   lse        float32 [S, B, R, H]: per-shard LSE, exactly -inf where empty;

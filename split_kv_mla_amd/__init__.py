@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     decode_args,
     load_library,
     mla_lse_combine,
+    mla_merge_states,
     mla_plan_capacity,
     mla_shard_decode_partial,
     mla_split_decode,

@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.mla_split_decode.restype = ctypes.c_int
     lib.mla_split_decode_timed.argtypes = lib.mla_split_decode.argtypes + [ctypes.c_void_p] * 3
     lib.mla_split_decode_timed.restype = ctypes.c_int
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.mla_merge_states.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -233,3 +237,45 @@ def mla_lse_combine(out_partial, lse, out=None, lse_final=None, want_lse_final=T
     _check(load_library().mla_lse_combine(_ptr(out_partial), _ptr(lse), S, B, R, H, _ptr(out),
                                           _ptr(lse_final), _stream(dev)))
     return out, lse_final
+
+
+_MERGE_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+def _lse_view(t, name, T, H, dev):
+    """A float32 [H, T] LSE view (any non-negative strides): its two strides."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 torch.Tensor")
+    if tuple(t.shape) != (H, T) or t.device != dev:
+        raise ValueError(f"{name} must be [{H}, {T}] on {dev}, got {tuple(t.shape)} on {t.device}")
+    return t.stride(0), t.stride(1)
+
+
+def mla_merge_states(prefix, prefix_lse, suffix, suffix_lse, out=None, out_lse=None, want_lse=True):
+    """Two-way merge of attention states by LSE: prefix, suffix [T, H, D]
+    (float32, bf16 or fp16, contiguous), LSEs float32 [H, T] views (any
+    strides).  `out` may be `prefix` or `suffix` itself and `out_lse` may be
+    `prefix_lse` or `suffix_lse` itself (in-place merge).
+
+    Returns (out [T, H, D], out_lse [H, T] or None).
+    """
+    if prefix.dim() != 3:
+        raise ValueError("prefix must be [T, H, D]")
+    T, H, D = prefix.shape
+    dev = prefix.device
+    if prefix.dtype not in _MERGE_DTYPES:
+        raise TypeError(f"unsupported dtype {prefix.dtype}")
+    _need(prefix, "prefix", prefix.dtype, device=dev)
+    _need(suffix, "suffix", prefix.dtype, (T, H, D), dev)
+    if out is None:
+        out = torch.empty_like(prefix)
+    _need(out, "out", prefix.dtype, (T, H, D), dev)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    p_sh, p_st = _lse_view(prefix_lse, "prefix_lse", T, H, dev)
+    s_sh, s_st = _lse_view(suffix_lse, "suffix_lse", T, H, dev)
+    o_sh, o_st = _lse_view(out_lse, "out_lse", T, H, dev) if out_lse is not None else (0, 0)
+    _check(load_library().mla_merge_states(
+        _ptr(out), _ptr(out_lse), o_sh, o_st, _ptr(prefix), _ptr(prefix_lse), p_sh, p_st,
+        _ptr(suffix), _ptr(suffix_lse), s_sh, s_st, T, H, D, _MERGE_DTYPES[prefix.dtype], _stream(dev)))
+    return out, out_lse

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_split_kv.so")
-SOURCES = [os.path.join(HERE, "csrc", "mla_split_kv.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "mla_split_kv.hip"), os.path.join(HERE, "csrc", "mla_merge.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "mla_kernels.h"), os.path.join(HERE, "csrc", "mla_plan.h"),
            os.path.join(ROOT, "include", "mla_split_kv.h")]
 
@@ -25,7 +25,8 @@ def command(out=LIB, extra=()):
             # keep packed-fp32 instructions out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-            *extra, *SOURCES, "-o", out]
+            # assembly output (-S) is one file: the decode kernels' translation unit
+            *extra, *(SOURCES[:1] if "-S" in extra else SOURCES), "-o", out]
 
 
 def build(verbose=False):

@@ -182,3 +182,28 @@ def test_batch_zero_returns_ok_without_launching():
     null = ctypes.c_void_p(0)
     assert lib.mla_split_decode(ctypes.byref(a), null, null, null, null, 0, null) == 0
     assert lib.mla_lse_combine(null, null, 8, 0, 1, 16, null, null, null) == 0
+
+
+def test_merge_states_rejects_bad_arguments_without_launching():
+    lib = m.load_library()
+    vp = ctypes.c_void_p
+
+    def call(out=0x10000, out_lse=0x90000, prefix=0x20000, p_lse=0xA0000, suffix=0x40000, s_lse=0xB0000,
+             T=4, H=6, D=128, dtype=1, strides=(4, 1)):
+        sh, st = strides
+        return lib.mla_merge_states(vp(out), vp(out_lse), sh, st, vp(prefix), vp(p_lse), sh, st, vp(suffix),
+                                    vp(s_lse), sh, st, T, H, D, dtype, vp(0))
+
+    assert call(T=0) == 0                        # nothing to do, nothing launched
+    assert call(T=0, prefix=0) == 0
+    assert call(dtype=3) == -1 and call(H=0) == -1 and call(D=0) == -1 and call(T=-1) == -1
+    assert call(prefix=0) == -1 and call(s_lse=0) == -1
+    assert call(strides=(-4, 1)) == -1
+    assert call(D=100) == -2                     # 200-byte rows are not a multiple of 16 bytes
+    assert call(prefix=0x20008) == -1            # payloads must be 16-byte aligned
+    assert call(out=0x20000 + 6 * 256) == -1     # output overlapping the prefix at another row
+    assert call(out_lse=0xA0000 + 4) == -1       # output LSE overlapping the prefix LSE, shifted
+    assert call(out_lse=0x10000 + 16) == -1      # output LSE inside the output payload
+    assert call(out_lse=0x20000 + 64) == -1      # output LSE inside the prefix payload
+    assert call(p_lse=0x10000 + 32) == -1        # output payload over the prefix LSE
+    assert call(D=1 << 16) == -2                 # rows above 64 KiB

@@ -9,5 +9,6 @@ from .gen import (  # noqa: F401
     long_context,
     verify,
     padded,
+    merge_inputs,
     STANDARD,
 )

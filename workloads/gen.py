@@ -219,3 +219,39 @@ STANDARD = {
     "verify": verify,
     "padded": padded,
 }
+
+
+# ---------------------------------------------------------------------------
+# Two-way merge inputs.
+# ---------------------------------------------------------------------------
+
+def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02):
+    """Prefix and suffix attention states for the two-way merge.
+
+    Returns float32 arrays prefix, suffix [T, H, D] of N(0, 1) values rounded
+    to ``dtype`` ("f32", "bf16" or "f16", so that they are exact in it) and
+    float32 LSEs prefix_lse, suffix_lse [H, T] drawn uniformly from [-3, 12];
+    each side's LSE is -inf with probability ``empty_frac`` and both are with
+    probability ``both_empty_frac``; payloads of sides with LSE -inf are NaN.
+    """
+    rng = np.random.default_rng(seed)
+    p = rng.standard_normal((T, H, D), dtype=np.float32)
+    s = rng.standard_normal((T, H, D), dtype=np.float32)
+    if dtype == "bf16":
+        p = (bf16_rne_bits(p).astype(np.uint32) << 16).view(np.float32)
+        s = (bf16_rne_bits(s).astype(np.uint32) << 16).view(np.float32)
+    elif dtype == "f16":
+        p = p.astype(np.float16).astype(np.float32)
+        s = s.astype(np.float16).astype(np.float32)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    lp = rng.uniform(-3.0, 12.0, size=(H, T)).astype(np.float32)
+    ls = rng.uniform(-3.0, 12.0, size=(H, T)).astype(np.float32)
+    lp[rng.random((H, T)) < empty_frac] = -np.inf
+    ls[rng.random((H, T)) < empty_frac] = -np.inf
+    both = rng.random((H, T)) < both_empty_frac
+    lp[both] = -np.inf
+    ls[both] = -np.inf
+    p[np.isneginf(lp).T] = np.nan
+    s[np.isneginf(ls).T] = np.nan
+    return {"prefix": p, "prefix_lse": lp, "suffix": s, "suffix_lse": ls}
