@@ -42,7 +42,10 @@
  * - Device-detected input faults (a block id outside [0, num_blocks) in a
  *   referenced table entry, seq_lens[b] outside [0, max_blocks_per_seq *
  *   block_size]) produce NaN in every output of the affected request rather
- *   than reading out of bounds.
+ *   than reading out of bounds or clamping (the PR 565 page's review-fix
+ *   commit text: a plan that cannot cover the pages it must read is rejected,
+ *   not clamped), and set a bit of the call's fault word: the first int32 of
+ *   the workspace, which mla_device_faults reads once the stream is done.
  */
 #ifndef MLA_SPLIT_KV_H
 #define MLA_SPLIT_KV_H
@@ -63,6 +66,14 @@ enum {
 };
 
 enum { MLA_HEAD_DIM = 576, MLA_V_DIM = 512 };
+
+/* Bits of a decode call's fault word. */
+enum {
+  MLA_FAULT_BLOCK_ID = 1, /* a referenced block_table entry outside [0, num_blocks)      */
+  MLA_FAULT_SEQ_LEN = 2,  /* seq_lens[b] < 0 or > max_blocks_per_seq * block_size       */
+  MLA_FAULT_PLAN = 4      /* the device work plan did not fit the workspace (never with a */
+                          /* workspace of mla_workspace_bytes(a) bytes)                  */
+};
 
 typedef struct mla_decode_args {
   const void* q;              /* device bf16 [B, R, H, 576]                              */
@@ -87,18 +98,27 @@ typedef struct mla_decode_args {
 size_t mla_workspace_bytes(const mla_decode_args* a);
 
 /* Partial attention of shards [shard_begin, shard_begin + shard_count): what
- * one DCP rank computes for its own shard(s).  Writes
+ * one DCP rank computes for its own shard(s) before the exchange (vLLM PR
+ * 50484 page, "Summary"; its prhub.com.cn summary, "implementation
+ * breakdown" step 4: every shard yields a partial output and its LSE, and an
+ * empty shard's LSE is set to -inf at the source).  Writes
  *   out_partial  float32 [shard_count, B, R, H, 512]: softmax over the shard's
  *                tokens; left undefined where the shard is empty for a row;
  *   lse          float32 [shard_count, B, R, H]: the shard's natural-log LSE,
  *                exactly -inf where the shard is empty for a row.
  * workspace: device memory of at least mla_workspace_bytes(a) bytes; its
- * contents on entry do not matter. */
+ * contents on entry do not matter; its first int32 is the call's fault word.
+ * Errors: MLA_ERR_INVALID_ARG (null pointer, bad shard range),
+ * MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
 int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count,
                              float* out_partial, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* LSE-weighted merge of S partial states (the DCP combine):
+/* LSE-weighted merge of S partial states: the DCP combine (vLLM PR 50484
+ * page, "Summary": the output/LSE reduction with empty-shard masking; its
+ * prhub.com.cn summary, "implementation breakdown" step 4: exp2 LSE-weighted
+ * merge, the consumer giving a -inf source zero weight without reading it;
+ * "key source excerpts": combine(latent_out, lse, seq_lens, ...)):
  *   out_partial  float32 [S, B, R, H, 512], lse float32 [S, B, R, H] (inputs);
  *   out          bf16 [B, R, H, 512]: sum_s w_s * out_partial[s] / sum_s w_s
  *                with w_s = exp2((lse_s - max_s lse_s) * log2(e)); sources
@@ -106,7 +126,9 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
  *                +0.0 where every source is empty;
  *   lse_final    float32 [B, R, H] or NULL: the merged natural-log LSE
  *                (-inf where every source is empty).
- * out may not alias out_partial. */
+ * out may not alias out_partial.  Nothing here is detected on the device (a
+ * NaN input LSE gives a NaN row).  Errors: MLA_ERR_INVALID_ARG (null
+ * pointer, non-positive sizes), MLA_ERR_HIP. */
 int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shards, int32_t batch,
                     int32_t rows, int32_t heads, void* out, float* lse_final, void* stream);
 
@@ -128,19 +150,28 @@ int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shar
  * an output and an input is rejected (MLA_ERR_INVALID_ARG), as are
  * misaligned pointers, negative strides, or dtype outside 0..2.  head_dim *
  * element size must be a multiple of 16 bytes and at most 64 KiB
- * (MLA_ERR_UNSUPPORTED).  out_lse's strides must give every row its own slot.
- * LSEs are expected finite or -inf.  tokens == 0 enqueues nothing. */
+ * (MLA_ERR_UNSUPPORTED).  out_lse's strides must give every (head, token)
+ * its own slot: ordered by stride, the dimensions longer than 1 must have
+ * strides s1 >= 1 and s2 >= s1 * (extent of the first), else
+ * MLA_ERR_INVALID_ARG.  LSEs are expected finite or -inf.  tokens == 0
+ * enqueues nothing. */
 int mla_merge_states(void* out, float* out_lse, int64_t out_lse_stride_head, int64_t out_lse_stride_token,
                      const void* prefix, const float* prefix_lse, int64_t prefix_lse_stride_head,
                      int64_t prefix_lse_stride_token, const void* suffix, const float* suffix_lse,
                      int64_t suffix_lse_stride_head, int64_t suffix_lse_stride_token, int32_t tokens,
                      int32_t heads, int32_t head_dim, int32_t dtype, void* stream);
 
-/* The whole path: partial attention of every shard, then the LSE combine.
+/* The whole path: partial attention of every shard, then the LSE combine
+ * (vLLM PR 50484 page, "Summary"; its prhub.com.cn summary, "key source
+ * excerpts": forward_mqa yields latent_out and lse, then the DCP manager's
+ * combine merges them; R > 1 rows share every KV tile: PR 565 page,
+ * "Summary").
  *   out        bf16 [B, R, H, 512]: attention over each row's whole KV;
  *   lse        float32 [S, B, R, H]: per-shard LSE, exactly -inf where empty;
  *   lse_final  float32 [B, R, H] or NULL: LSE over all shards.
- * workspace as for mla_shard_decode_partial. */
+ * workspace as for mla_shard_decode_partial (its first int32 is the call's
+ * fault word).  Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
 int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse_final,
                      void* workspace, size_t workspace_bytes, void* stream);
 
@@ -151,6 +182,13 @@ int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse
 int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final,
                            void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
                            void* ev_mid, void* ev_end);
+
+/* The fault word (MLA_FAULT_* bits) of the last decode call enqueued on
+ * `stream` with `workspace`: waits for the stream, then copies the word to
+ * *faults.  0 means the call met no device-detected fault.  This is the one
+ * call that synchronises.  Errors: MLA_ERR_INVALID_ARG (null pointer),
+ * MLA_ERR_HIP. */
+int mla_device_faults(const void* workspace, void* stream, int32_t* faults);
 
 /* A static string naming a status code. */
 const char* mla_status_string(int status);

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     MlaError,
     decode_args,
     load_library,
+    mla_device_faults,
     mla_lse_combine,
     mla_merge_states,
     mla_plan_capacity,

@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_merge_states.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
     lib.mla_merge_states.restype = ctypes.c_int
+    lib.mla_device_faults.argtypes = [ctypes.c_void_p, ctypes.c_void_p, P(ctypes.c_int32)]
+    lib.mla_device_faults.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -147,6 +149,18 @@ def mla_plan_capacity(args: MlaDecodeArgs, shard_count=None):
     sc = args.num_shards if shard_count is None else shard_count
     n = load_library().mla_plan_capacity(ctypes.byref(args), sc, ctypes.byref(rg))
     return int(n), int(rg.value)
+
+
+FAULT_BLOCK_ID, FAULT_SEQ_LEN, FAULT_PLAN = 1, 2, 4
+
+
+def mla_device_faults(workspace) -> int:
+    """Fault word (FAULT_* bits) of the last decode call that used `workspace`
+    on the current stream; waits for that stream."""
+    _need(workspace, "workspace", torch.uint8)
+    f = ctypes.c_int32(-1)
+    _check(load_library().mla_device_faults(_ptr(workspace), _stream(workspace.device), ctypes.byref(f)))
+    return int(f.value)
 
 
 def new_workspace(args: MlaDecodeArgs, device):
@@ -242,13 +256,19 @@ def mla_lse_combine(out_partial, lse, out=None, lse_final=None, want_lse_final=T
 _MERGE_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 
-def _lse_view(t, name, T, H, dev):
-    """A float32 [H, T] LSE view (any non-negative strides): its two strides."""
+def _lse_view(t, name, T, H, dev, distinct=False):
+    """A float32 [H, T] LSE view (any non-negative strides): its two strides.
+    With `distinct`, the view must give every (head, token) its own element."""
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
         raise TypeError(f"{name} must be a float32 torch.Tensor")
     if tuple(t.shape) != (H, T) or t.device != dev:
         raise ValueError(f"{name} must be [{H}, {T}] on {dev}, got {tuple(t.shape)} on {t.device}")
-    return t.stride(0), t.stride(1)
+    sh, st = t.stride(0), t.stride(1)
+    if distinct:
+        dims = sorted((s, n) for s, n in ((sh, H), (st, T)) if n > 1)
+        if (dims and dims[0][0] < 1) or (len(dims) == 2 and dims[1][0] < dims[0][0] * dims[0][1]):
+            raise ValueError(f"{name} must give every (head, token) its own element, strides {(sh, st)}")
+    return sh, st
 
 
 def mla_merge_states(prefix, prefix_lse, suffix, suffix_lse, out=None, out_lse=None, want_lse=True):
@@ -274,7 +294,7 @@ def mla_merge_states(prefix, prefix_lse, suffix, suffix_lse, out=None, out_lse=N
         out_lse = torch.empty((H, T), dtype=torch.float32, device=dev)
     p_sh, p_st = _lse_view(prefix_lse, "prefix_lse", T, H, dev)
     s_sh, s_st = _lse_view(suffix_lse, "suffix_lse", T, H, dev)
-    o_sh, o_st = _lse_view(out_lse, "out_lse", T, H, dev) if out_lse is not None else (0, 0)
+    o_sh, o_st = _lse_view(out_lse, "out_lse", T, H, dev, distinct=True) if out_lse is not None else (0, 0)
     _check(load_library().mla_merge_states(
         _ptr(out), _ptr(out_lse), o_sh, o_st, _ptr(prefix), _ptr(prefix_lse), p_sh, p_st,
         _ptr(suffix), _ptr(suffix_lse), s_sh, s_st, T, H, D, _MERGE_DTYPES[prefix.dtype], _stream(dev)))

@@ -79,8 +79,10 @@ struct DecodeParams {
   const int32_t* seq_lens;   // [B]
   void* part_o;              // [items_cap, rows_total] slots of 512 fp32 (or 512 fp16 in the first half)
   float* part_lse;           // [items_cap, rows_total]
-  uint8_t* part_fmt;         // [items_cap, rows_total]: 1 = the slot holds fp16
+  uint8_t* part_fmt;         // [items_cap, rows_total]: bit 0 = the slot holds fp16, bit 1 = a
+                             // referenced block id was out of range (the LSE is NaN)
   int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, cell size U
+  int32_t* faults;           // fault word of the call: cleared here, set by the combine
   int32_t B, R, H, rows_total, row_groups;
   int32_t num_blocks, bs_log2, max_blocks, cap_tokens;
   int32_t S, I, shard_begin, shard_count, pairs;
@@ -455,6 +457,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
 
   const int G = p.row_groups;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
+  // The call's fault word starts clear; the combine kernel, which runs after
+  // this kernel has completed, sets its bits.
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.faults = 0;
 
   // One request: its length comes through the scalar cache, issued before the
   // query copy so that it does not queue behind those vector loads.
@@ -874,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
     const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
-    if (live && g == 0) p.part_fmt[prow] = as_half ? 1 : 0;
+    if (row_ok && g == 0 && (live || bad)) p.part_fmt[prow] = bad ? 2 : (as_half ? 1 : 0);
     // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3].
     // Rows leave through the idle ring, transposed so that a store writes a
     // whole 1 KiB piece of a row (the scattered pieces of the register layout
@@ -951,6 +956,11 @@ enum CombineMode : int32_t {
   kCombineShards = 2,  // merge caller-provided shard partials: bf16 out, lse_final
 };
 
+// Bits of a call's fault word (the first word of its workspace).
+constexpr int32_t kFaultBlockId = 1;  // a referenced block-table entry outside [0, num_blocks)
+constexpr int32_t kFaultSeqLen = 2;   // seq_lens[b] outside [0, max_blocks_per_seq * block_size]
+constexpr int32_t kFaultPlan = 4;     // the work plan did not fit the workspace's item slots
+
 struct CombineParams {
   const void* src_o;        // items: [items_cap, rows, 512]; shards: [S, B, rows, 512] fp32
   const float* src_lse;     // items: [items_cap, rows]; shards: [S, B, rows]
@@ -962,6 +972,7 @@ struct CombineParams {
   void* out;                // bf16 [B, rows, 512] or fp32 [shard_count, B, rows, 512]
   float* lse_shard;         // [shard_count, B, rows]
   float* lse_final;         // [B, rows] or NULL
+  int32_t* faults;          // fault word of the call (item modes), or NULL
   int32_t B, rows, shard_count, mode;
 };
 
@@ -1012,6 +1023,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   int i0, i1;
   size_t o_stride, l_stride, o_base, l_base;
   bool bad = false;
+  int fault = 0;  // kFault* bits found for this row
   if (p.mode == kCombineShards) {
     i0 = 0;
     i1 = p.shard_count;
@@ -1028,13 +1040,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     if (i0 < 0 || i1 < i0 || i1 > p.items_cap) {  // a plan that does not fit its slots: report, never read
       i0 = i1 = 0;
       bad = true;
+      fault |= kFaultPlan;
     }
     l_stride = (size_t)p.rows;
     l_base = row;
     o_stride = l_stride * kVDim;
     o_base = (size_t)row * kVDim;
     const int32_t L = p.seq_lens[b];
-    bad = bad || L < 0 || L > p.cap_tokens;
+    if (L < 0 || L > p.cap_tokens) {
+      bad = true;
+      fault |= kFaultSeqLen;
+    }
   }
   const int n = i1 - i0;
   const bool staged = n <= kCombineLdsSources;
@@ -1047,16 +1063,21 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
   // pass 1: stage the source LSEs, their max, and the total weight
   float m = -INFINITY;
+  int fmt_bits = 0;
   for (int i = tid; i < n; i += kThreads) {
     const float x = p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
+    if (x != -INFINITY) fmt_bits |= fmt_at(i);
     if (staged) {
       src_lse[i] = x;
       src_fmt[i] = (uint8_t)fmt_at(i);
     }
     m = nan_max(m, x);
   }
+  // a source whose block-table window named a block outside the cache (its LSE is NaN)
+  if (__any(fmt_bits & 2)) fault |= kFaultBlockId;
   m = block_reduce(m, true, red);  // its barriers also publish src_lse
   bad = bad || (m != m);
+  if (p.faults && fault && (threadIdx.x & 63) == 0) atomicOr(p.faults, fault);
   const bool empty = (m == -INFINITY);
   float wsum = 0.f;
   if (!bad && !empty)
@@ -1077,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       if (x == -INFINITY) continue;  // empty source: its payload is never read
       const float w = __builtin_amdgcn_exp2f((x - m) * kLog2e);
       const size_t off = o_base + (size_t)(i0 + i) * o_stride + col;  // in floats
-      if (staged ? src_fmt[i] : fmt_at(i)) {
+      if ((staged ? src_fmt[i] : fmt_at(i)) & 1) {
         // an fp16 slot: the same columns in the first half of the slot
         const f16x8 hv = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.src_o) + 2 * off - col);
 #pragma unroll
@@ -1127,6 +1148,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   }
   if (tid == 0 && p.lse_final) p.lse_final[orow] = lse_all;
   if (p.mode != kCombineItems) return;
+  if (bad) {  // the published plan may not fit the item slots: never index through it
+    if (tid < p.shard_count) p.lse_shard[(size_t)tid * p.B * p.rows + orow] = qnan;
+    for (int s = kThreads + tid; s < p.shard_count; s += kThreads) p.lse_shard[(size_t)s * p.B * p.rows + orow] = qnan;
+    return;
+  }
   // per-shard LSE over each shard's items: one wavefront per shard
   const int wave = tid >> 6, lane = tid & 63;
   for (int s = wave; s < p.shard_count; s += kThreads / 64) {

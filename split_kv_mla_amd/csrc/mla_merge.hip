@@ -17,6 +17,15 @@ Span lse_span(const float* base, int64_t sh, int64_t st, int32_t H, int32_t T) {
   return {lo, lo + (uintptr_t)(((H - 1) * sh + (T - 1) * st + 1) * (int64_t)sizeof(float))};
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Whether (h, t) -> h * sh + t * st gives every (head, token) its own element:
+// ordered by stride, the dimensions longer than 1 must not interleave (the
+// smaller stride at least 1, the larger at least the smaller times its extent).
+bool distinct_slots(int64_t sh, int64_t st, int32_t H, int32_t T) {
+  if (H == 1 || T == 1) return (H == 1 ? st : sh) >= 1 || (H == 1 && T == 1);
+  if (sh <= st) return sh >= 1 && st / H >= sh;
+  return st >= 1 && sh / T >= st;
+}
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
@@ -51,6 +60,8 @@ int mla_merge_states(void* out, float* out_lse, int64_t out_lse_stride_head, int
     const uintptr_t i0 = reinterpret_cast<uintptr_t>(in);
     if (i0 != o0 && overlap(po, Span{i0, i0 + (uintptr_t)(rows * row_bytes)})) return MLA_ERR_INVALID_ARG;
   }
+  if (out_lse && !distinct_slots(out_lse_stride_head, out_lse_stride_token, heads, tokens))
+    return MLA_ERR_INVALID_ARG;  // rows of different wavefronts would share an LSE slot
   if (out_lse) {
     const Span lo = lse_span(out_lse, out_lse_stride_head, out_lse_stride_token, heads, tokens);
     const bool same_p = out_lse == prefix_lse && out_lse_stride_head == prefix_lse_stride_head &&

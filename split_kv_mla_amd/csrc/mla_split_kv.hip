@@ -50,20 +50,25 @@ int check_args(const mla_decode_args* a) {
   return MLA_OK;
 }
 
+// The workspace opens with a header whose first int32 is the call's fault
+// word (mla_device_faults reads it); the plan and the item partials follow.
+constexpr size_t kHeaderBytes = 256;
+
 struct Plan {
   int32_t pairs, row_groups, items_cap, tpi_max, slots;
   size_t plan_bytes, lse_bytes, fmt_bytes, o_bytes;
-  size_t total() const { return plan_bytes + lse_bytes + fmt_bytes + o_bytes; }
+  size_t total() const { return kHeaderBytes + plan_bytes + lse_bytes + fmt_bytes + o_bytes; }
 };
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Capacity of the item plan.  The device splits the launch's cost axis (tiles
-// plus kPieceCost per non-empty pair) into `slots` ranges of m cells of U
-// tiles, m = ceil(ceil(T / slots) / tpi_max); the cells cover at most
-// slots * m positions and each pair adds at most one item to the cells it
-// touches, so slots * m + pairs items always fit.  T is at most the cost of
-// every request filling its block table.
+// plus kPieceCost per non-empty (request, shard) pair) into `slots` ranges of
+// m cells of U tiles, m = ceil(ceil(T / slots) / tpi_max); the cells cover at
+// most slots * m positions and each pair adds at most one item to the cells it
+// touches, so slots * m + pairs items always fit.  m grows with T, and T is at
+// most the cost of every request filling its block table: per request, the
+// tiles of its shard_count shards plus kPieceCost for each of them.
 Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_count) {
   Plan p{};
   const int32_t rows_total = a->rows * a->heads;
@@ -75,7 +80,7 @@ Plan make_plan(const mla_decode_args* a, int32_t shard_begin, int32_t shard_coun
   int64_t cap_tiles = 0;
   for (int32_t s = shard_begin; s < shard_begin + shard_count; ++s)
     cap_tiles += ceil_div(mla::local_len(cap_tokens, a->num_shards, a->interleave, s), mla::kTile);
-  const int64_t cap_cost = (cap_tiles + mla::kPieceCost) * a->batch;
+  const int64_t cap_cost = (cap_tiles + (int64_t)shard_count * mla::kPieceCost) * a->batch;
   const int64_t wmin = std::max<int64_t>(1, (cap_cost + p.slots - 1) / p.slots);
   const int64_t m = (wmin + p.tpi_max - 1) / p.tpi_max;
   p.items_cap = (int32_t)std::min<int64_t>((int64_t)p.slots * m + p.pairs, INT32_MAX);
@@ -93,7 +98,8 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   p.kv = static_cast<const uint16_t*>(a->kv_cache);
   p.table = a->block_table;
   p.seq_lens = a->seq_lens;
-  char* w = static_cast<char*>(ws);
+  p.faults = static_cast<int32_t*>(ws);
+  char* w = static_cast<char*>(ws) + kHeaderBytes;
   p.plan_out = reinterpret_cast<int32_t*>(w);
   p.part_lse = reinterpret_cast<float*>(w + pl.plan_bytes);
   p.part_fmt = reinterpret_cast<uint8_t*>(w + pl.plan_bytes + pl.lse_bytes);
@@ -186,6 +192,7 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   c.out = out_partial;
   c.lse_shard = lse;
   c.lse_final = nullptr;
+  c.faults = p.faults;
   c.B = a->batch;
   c.rows = p.rows_total;
   c.shard_count = shard_count;
@@ -210,6 +217,7 @@ int mla_lse_combine(const float* out_partial, const float* lse, int32_t num_shar
   c.out = out;
   c.lse_shard = nullptr;
   c.lse_final = lse_final;
+  c.faults = nullptr;
   c.B = batch;
   c.rows = rows * heads;
   c.shard_count = num_shards;
@@ -241,6 +249,7 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   c.out = out;
   c.lse_shard = lse;
   c.lse_final = lse_final;
+  c.faults = p.faults;
   c.B = a->batch;
   c.rows = p.rows_total;
   c.shard_count = a->num_shards;
@@ -254,6 +263,14 @@ int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse
                      size_t workspace_bytes, void* stream) {
   return mla_split_decode_timed(a, out, lse, lse_final, workspace, workspace_bytes, stream, nullptr, nullptr,
                                 nullptr);
+}
+
+int mla_device_faults(const void* workspace, void* stream, int32_t* faults) {
+  if (!workspace || !faults) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MLA_ERR_HIP;
+  if (hipMemcpy(faults, workspace, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
 }
 
 const char* mla_status_string(int status) {

@@ -137,17 +137,47 @@ def test_even_split_covers_every_tile_once_with_balanced_slots():
             assert sum(t1 - t0 for _, _, _, t0, t1 in mine) <= W
 
 
+def _plan_items_when_full(B, R, S, I, bs, maxb):
+    """(items of the modelled device plan with every request filling its
+    table, the library's capacity)."""
+    a = _args(B=B, R=R, S=S, I=I, bs=bs, max_blocks=maxb)
+    cap, groups = m.mla_plan_capacity(a)
+    slots = 8 * (32 // groups)
+    L = maxb * bs
+    tiles = [(((L // (S * I)) * I + min(I, max(0, L % (S * I) - s * I))) + 31) // 32 for s in range(S)] * B
+    U, W, T, pieces = _even_split(tiles, slots, _tpi_max(S, I, bs))
+    return len(pieces), cap
+
+
 def test_plan_capacity_covers_longest_requests():
     """Items of the device plan when every request fills its table never exceed the capacity."""
     for S, I, bs, maxb, R in [(8, 1, 64, 2048, 1), (8, 16, 64, 2048, 4), (3, 5, 16, 100, 1), (1, 1, 1, 4000, 2),
                               (16, 64, 128, 1024, 3)]:
-        a = _args(B=3, R=R, S=S, I=I, bs=bs, max_blocks=maxb)
-        cap, groups = m.mla_plan_capacity(a)
-        slots = 8 * (32 // groups)
-        L = maxb * bs
-        tiles = [(((L // (S * I)) * I + min(I, max(0, L % (S * I) - s * I))) + 31) // 32 for s in range(S)] * 3
-        U, W, T, pieces = _even_split(tiles, slots, _tpi_max(S, I, bs))
-        assert len(pieces) <= cap, (S, I, bs, maxb, len(pieces), cap)
+        items, cap = _plan_items_when_full(3, R, S, I, bs, maxb)
+        assert items <= cap, (S, I, bs, maxb, items, cap)
+
+
+@pytest.mark.parametrize("B,R,maxb", [(16, 4, 981), (64, 1, 2001), (8, 1, 8133), (128, 1, 300),
+                                      (16, 4, 2048), (64, 1, 2048)])
+def test_plan_capacity_many_requests(B, R, maxb):
+    """Batches where the per-pair item charge dominates the cost axis: the
+    capacity counts it for every (request, shard) pair."""
+    items, cap = _plan_items_when_full(B, R, 8, 16 if R == 4 else 1, 64, maxb)
+    assert items <= cap, (B, R, maxb, items, cap)
+
+
+def test_plan_capacity_across_cell_count_changes():
+    """Block-table widths on both sides of every point where the number of
+    cells per slot (m) steps up."""
+    S, I, bs, R, B = 8, 1, 64, 1, 16
+    tpi = _tpi_max(S, I, bs)
+    slots = 8 * 32
+    for k in (1, 2, 3):
+        # the cost axis reaches k * slots * tpi_max near this table width
+        width = max(1, (k * slots * tpi // B - S * PIECE_COST) * 32 * S // bs)
+        for maxb in (width - 2, width - 1, width, width + 1, width + 2):
+            items, cap = _plan_items_when_full(B, R, S, I, bs, maxb)
+            assert items <= cap, (k, maxb, items, cap)
 
 
 def test_bad_arguments_return_errors_without_launching():
@@ -207,3 +237,38 @@ def test_merge_states_rejects_bad_arguments_without_launching():
     assert call(out_lse=0x20000 + 64) == -1      # output LSE inside the prefix payload
     assert call(p_lse=0x10000 + 32) == -1        # output payload over the prefix LSE
     assert call(D=1 << 16) == -2                 # rows above 64 KiB
+
+
+def test_merge_states_rejects_aliasing_output_lse_strides():
+    """out_lse strides that give two (head, token) pairs one element would
+    let rows of different wavefronts race on it."""
+    lib = m.load_library()
+    vp = ctypes.c_void_p
+
+    def call(o_strides, T=4, H=6, p_lse=0xA0000, out_lse=0x90000):
+        sh, st = o_strides
+        return lib.mla_merge_states(vp(0x10000), vp(out_lse), sh, st, vp(0x20000), vp(p_lse), 4, 1, vp(0x40000),
+                                    vp(0xB0000), 4, 1, T, H, 128, 1, vp(0))
+
+    for bad in [(0, 1), (1, 0), (0, 0), (2, 1), (1, 2), (3, 2)]:
+        assert call(bad) == -1, bad
+    # the same aliasing view as the prefix LSE, in place: still rejected
+    assert call((0, 1), p_lse=0x90000) == -1
+
+
+def test_device_faults_rejects_null_pointers():
+    lib = m.load_library()
+    f = ctypes.c_int32(0)
+    assert lib.mla_device_faults(ctypes.c_void_p(0), ctypes.c_void_p(0), ctypes.byref(f)) == -1
+    assert lib.mla_device_faults(ctypes.c_void_p(0x1000), ctypes.c_void_p(0), None) == -1
+
+
+def test_workspace_opens_with_the_fault_word_header():
+    """The workspace holds a 256-byte header (the fault word) before the plan
+    and the item partials."""
+    a = _args(B=1)
+    items, _ = m.mla_plan_capacity(a)
+    rows = a.rows * a.heads
+    body = 256 * (-(-4 * (a.batch * a.num_shards + 2) // 256)) + 256 * (-(-4 * items * rows // 256)) \
+        + 256 * (-(-items * rows // 256)) + 256 * (-(-4 * items * rows * 512 // 256))
+    assert m.mla_workspace_bytes(a) == 256 + body

@@ -126,3 +126,25 @@ def test_merge_states_without_lse_output_and_empty_input():
     zl = torch.empty((2, 0), device="cuda")
     out, lse = m.mla_merge_states(z, zl, z, zl)
     assert out.shape == (0, 2, 64) and lse.shape == (2, 0)
+
+
+@pytest.mark.parametrize("gap", [104.0, 300.0, 1000.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_states_far_apart_lses(gap, dtype):
+    """LSEs 104 to 1000 nats apart: the weaker side's float32 weight underflows
+    to zero (or a subnormal), so the stronger side comes back within the
+    output's rounding, its LSE unchanged; in place still equals disjoint."""
+    T, H, D = 1024, 6, 128
+    inp = merge_inputs(T, H, D, dtype, seed=int(gap) + (dtype == "f32"), gap=gap)
+    m = _lib()
+    p, s = _dev(inp["prefix"], TORCH[dtype]), _dev(inp["suffix"], TORCH[dtype])
+    lp, ls = _dev(inp["prefix_lse"]), _dev(inp["suffix_lse"])
+    _say(f"[merge] LSE gap {gap} {dtype}")
+    out, lse = m.mla_merge_states(p, lp, s, ls)
+    torch.cuda.synchronize()
+    _check(out, lse, inp, dtype, f"gap {gap}")
+    got, got_lse = m.mla_merge_states(p, lp, s, ls, out=p, out_lse=lp)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16) if dtype != "f32" else got.view(torch.int32),
+                       out.view(torch.int16) if dtype != "f32" else out.view(torch.int32))
+    assert torch.equal(got_lse.view(torch.int32), lse.view(torch.int32))

@@ -267,6 +267,7 @@ def test_shard_map_against_dealing():
             for n in list(range(0, 200)) + [511, 1000, 4095]:
                 owner = _brute.deal_tokens(n, S, I)
                 sets = oracle.shard_token_sets(n, S, I)
+                assert [oracle.shard_of_token(t, S, I) for t in range(n)] == owner
                 for s in range(S):
                     members = [t for t in range(n) if owner[t] == s]
                     assert sets[s].tolist() == members
@@ -382,3 +383,24 @@ def test_merge_states_closed_form_equal_lse():
     p, s = np.full((1, 1, 128), 3.0), np.full((1, 1, 128), -1.0)
     out, lse = oracle.merge_states_oracle(p, np.array([[0.5]]), s, np.array([[0.5]]))
     assert np.all(out == 1.0) and lse[0, 0] == pytest.approx(0.5 + math.log(2.0), abs=1e-15)
+
+
+@pytest.mark.parametrize("gap", [104.0, 300.0, 1000.0])
+def test_merge_states_far_apart_lses(gap):
+    """LSEs far apart: the weaker side's weight exp(-gap) is below the double
+    range's resolution at 1 (gap > 37) or underflows outright (gap > 745), so
+    the merge returns the stronger side's state, and its LSE grows by
+    ln(1 + exp(-gap)) < 1e-16, i.e. not at all."""
+    rng = np.random.default_rng(int(gap))
+    p = rng.standard_normal((3, 2, 128))
+    q = rng.standard_normal((3, 2, 128))
+    lp = np.array([[5.0, -2.0, 7.0], [0.0, 1.0, -gap]])
+    ls = lp - gap
+    ls[1, 2] = 0.0  # here the suffix is the stronger side
+    out, lse = oracle.merge_states_oracle(p, lp, q, ls)
+    for t in range(3):
+        for h in range(2):
+            strong_prefix = lp[h, t] > ls[h, t]
+            want = p[t, h] if strong_prefix else q[t, h]
+            np.testing.assert_allclose(out[t, h], want, rtol=4e-16, atol=0)
+            assert lse[h, t] == max(lp[h, t], ls[h, t])

@@ -225,7 +225,7 @@ STANDARD = {
 # Two-way merge inputs.
 # ---------------------------------------------------------------------------
 
-def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02):
+def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02, gap=None):
     """Prefix and suffix attention states for the two-way merge.
 
     Returns float32 arrays prefix, suffix [T, H, D] of N(0, 1) values rounded
@@ -233,6 +233,8 @@ def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02):
     float32 LSEs prefix_lse, suffix_lse [H, T] drawn uniformly from [-3, 12];
     each side's LSE is -inf with probability ``empty_frac`` and both are with
     probability ``both_empty_frac``; payloads of sides with LSE -inf are NaN.
+    With ``gap``, the suffix LSE is instead the prefix LSE plus or minus
+    ``gap`` (sign drawn per row), so that one side's weight underflows.
     """
     rng = np.random.default_rng(seed)
     p = rng.standard_normal((T, H, D), dtype=np.float32)
@@ -247,6 +249,9 @@ def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02):
         raise ValueError(dtype)
     lp = rng.uniform(-3.0, 12.0, size=(H, T)).astype(np.float32)
     ls = rng.uniform(-3.0, 12.0, size=(H, T)).astype(np.float32)
+    if gap is not None:
+        sign = np.where(rng.random((H, T)) < 0.5, -1.0, 1.0)
+        ls = (lp.astype(np.float64) + sign * gap).astype(np.float32)
     lp[rng.random((H, T)) < empty_frac] = -np.inf
     ls[rng.random((H, T)) < empty_frac] = -np.inf
     both = rng.random((H, T)) < both_empty_frac
