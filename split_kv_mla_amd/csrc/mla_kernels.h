@@ -405,10 +405,12 @@ __device__ __forceinline__ void mfma_vgpr_done(f32x16& s) { asm volatile("s_nop 
 // 16 bytes per lane stored with system-scope coherence (sc0 sc1): written
 // through to memory rather than left dirty in this XCD's L2, so the end of
 // the kernel has less to write back before the combine may start.  Used for
-// the whole 1 KiB partial rows; the scattered pieces of fp32 rows are far
-// slower this way and keep ordinary stores.
+// the whole 1 KiB partial rows.  The two wait states after the store cover
+// the VMEM store-data hazard: the compiler does not see an assembly store,
+// and a store of more than 8 bytes reads its data registers after issue, so
+// the very next VALU instruction must not overwrite them.
 __device__ __forceinline__ void store_through(void* ptr, const f32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(ptr), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(ptr), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {

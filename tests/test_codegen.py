@@ -37,7 +37,7 @@ def test_m0_written_only_by_the_lds_dma_helpers(asm):
         x = _code(line)
         if not re.search(r"\bm0\b", x):
             continue
-        assert re.fullmatch(r"s_mov_b32 m0, s\d+", x), f"line {i + 1}: {x}"
+        assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", x), f"line {i + 1}: {x}"
         nxt = [_code(y) for y in asm[i + 1:i + 3]]
         assert nxt[0] == "s_nop 0" and nxt[1].startswith("global_load_lds_dword"), f"line {i + 1}: {nxt}"
         seen += 1
@@ -84,3 +84,32 @@ def test_vgpr_form_products_are_read_after_12_wait_states(asm):
 def test_no_packed_fp32_instructions(asm):
     hits = [i + 1 for i, line in enumerate(asm) if re.search(r"\bv_pk_(add|mul|fma)_f32\b", _code(line))]
     assert not hits, hits[:10]
+
+
+def test_wide_store_data_is_not_overwritten_at_once(asm):
+    """A global store of more than 8 bytes reads its data registers after it
+    issues: neither of the next two instructions may write them (the
+    compiler cannot see this for the stores written as assembly)."""
+    checked = 0
+    for i, line in enumerate(asm):
+        m = re.match(r"\s*global_store_dwordx(?:3|4)\s+v\[\d+:\d+\],\s*v\[(\d+):(\d+)\]", line)
+        if not m:
+            continue
+        data = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        checked += 1
+        seen = 0
+        for j in range(i + 1, min(len(asm), i + 40)):
+            x = _code(asm[j])
+            if not x or x.startswith("."):
+                continue
+            n = re.match(r"s_nop\s+(\d+)", x)
+            if n:
+                seen += int(n.group(1)) + 1
+            else:
+                dst = x.split(None, 1)[1].split(",")[0] if " " in x else ""
+                if x.startswith("v_") and _regs(dst) & data:
+                    assert seen >= 2, f"line {i + 1} -> {j + 1}: {x}"
+                seen += 1
+            if seen >= 2:
+                break
+    assert checked > 0
