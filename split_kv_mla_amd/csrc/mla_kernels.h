@@ -78,8 +78,8 @@ struct DecodeParams {
   const int32_t* table;      // [B, max_blocks]
   const int32_t* seq_lens;   // [B]
   void* part_o;              // [items_cap, rows_total] slots of 512 fp32 (or 512 fp16 in the first half)
-  float* part_lse;           // [items_cap, rows_total]
-  uint8_t* part_fmt;         // [items_cap, rows_total]: bit 0 = the slot holds fp16, bit 1 = a
+  float* part_lse;           // [rows_total, items_cap]: a row's item LSEs side by side
+  uint8_t* part_fmt;         // [rows_total, items_cap]: bit 0 = the slot holds fp16, bit 1 = a
                              // referenced block id was out of range (the LSE is NaN)
   int32_t* plan_out;         // [pairs + 2]: item start per pair, total items, cell size U
   int32_t* faults;           // fault word of the call: cleared here, set by the combine
@@ -865,10 +865,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const size_t prow = (size_t)item * p.rows_total + row;
+    const size_t lrow = (size_t)row * p.items_cap + item;  // the row's LSE and format of this item
     float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (bad) lse = __builtin_nanf("");
-    if (row_ok && g == 0) p.part_lse[prow] = lse;
+    if (row_ok && g == 0) p.part_lse[lrow] = lse;
     const bool live = row_ok && l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
     // The row's largest |o| picks its storage: fp16 when it is at most
@@ -881,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
     const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
-    if (row_ok && g == 0 && (live || bad)) p.part_fmt[prow] = bad ? 2 : (as_half ? 1 : 0);
+    if (row_ok && g == 0 && (live || bad)) p.part_fmt[lrow] = bad ? 2 : (as_half ? 1 : 0);
     // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3].
     // Rows leave through the idle ring, transposed so that a store writes a
     // whole 1 KiB piece of a row (the scattered pieces of the register layout
@@ -965,8 +965,8 @@ constexpr int32_t kFaultPlan = 4;     // the work plan did not fit the workspace
 
 struct CombineParams {
   const void* src_o;        // items: [items_cap, rows, 512]; shards: [S, B, rows, 512] fp32
-  const float* src_lse;     // items: [items_cap, rows]; shards: [S, B, rows]
-  const uint8_t* src_fmt;   // items: [items_cap, rows], 1 = fp16 slot; NULL = all fp32
+  const float* src_lse;     // items: [rows, items_cap]; shards: [S, B, rows]
+  const uint8_t* src_fmt;   // items: [rows, items_cap], 1 = fp16 slot; NULL = all fp32
   const int32_t* plan;      // [pairs + 2] from the partial kernel (item modes)
   const int32_t* seq_lens;  // [B] (item modes; NULL in kCombineShards)
   int32_t cap_tokens;
@@ -1044,9 +1044,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       bad = true;
       fault |= kFaultPlan;
     }
-    l_stride = (size_t)p.rows;
-    l_base = row;
-    o_stride = l_stride * kVDim;
+    l_stride = 1;  // a row's item LSEs lie side by side
+    l_base = (size_t)row * p.items_cap;
+    o_stride = (size_t)p.rows * kVDim;
     o_base = (size_t)row * kVDim;
     const int32_t L = p.seq_lens[b];
     if (L < 0 || L > p.cap_tokens) {
