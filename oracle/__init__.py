@@ -21,4 +21,9 @@ from .mla_oracle import (  # noqa: F401
     lse_combine_oracle,
     merge_states_oracle,
     padding_row_mask,
+    local_index_of_token,
+    chunked_context_alignment,
+    align_chunked_context_workspace,
+    context_chunk_plan,
+    gather_context_chunk_oracle,
 )

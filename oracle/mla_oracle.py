@@ -84,8 +84,9 @@ def row_length(seq_len: int, R: int, r: int, causal: bool) -> int:
     return max(n, 0)
 
 
-def shard_of_token(t: int, S: int, I: int) -> int:
-    """Shard holding global token position t: round-robin in units of I."""
+def shard_of_token(t, S: int, I: int):
+    """Shard holding global token position t (an int or an integer array):
+    round-robin in units of I."""
     return (t // I) % S
 
 
@@ -252,3 +253,106 @@ def padding_row_mask(seq_lens, query_start_loc):
     qsl = np.asarray(query_start_loc)
     qlens = qsl[1:] - qsl[:-1]
     return np.repeat(seq_lens == 0, qlens)
+
+
+# ---------------------------------------------------------------------------
+# Chunked-context KV gather: the prefill side of decode context parallelism.
+#
+# A prefill whose request already has a cached context attends to that
+# context chunk by chunk; each chunk's KV rows are first gathered into a
+# contiguous workspace in global token order.  Under DCP every shard holds
+# only its own share of the context in its own paged cache, so the gather
+# reassembles the chunk from the S shard-local caches ("[Kimi-K3] DCP
+# support" PR 50484 page, "Summary": the chunked-context KV gather; the
+# prhub.com.cn summary, "implementation breakdown" step 2, the prefill
+# chunked context routed through the KV gather, and step 3, the workspace
+# alignment).
+#
+# Readings taken where the pages are silent:
+# * workspace sizes count rows (one 576-wide cache row per token);
+# * shard s's local token j is the j-th token the round-robin deal gives it,
+#   stored at slot j % block_size of block local_tables[s, b, j // block_size];
+#   on one device the shards' local blocks live in one pool of physical blocks;
+# * the chunk length C is the same for every request: the largest multiple of
+#   the alignment with n * C rows fitting the workspace, n the number of
+#   requests with a nonzero context; chunk k of a request covers its context
+#   positions [k * C, min((k + 1) * C, context_len));
+# * a chunk's rows are packed request after request, each in global order.
+# ---------------------------------------------------------------------------
+
+def local_index_of_token(t, S: int, I: int):
+    """Index of global token t (an int or an integer array) in its shard's
+    local sequence: the complete rounds of S * I tokens before t give I
+    tokens each to every shard, and t is the (t mod I)-th token of its own
+    interleave unit."""
+    return (t // (S * I)) * I + t % I
+
+
+def chunked_context_alignment(block_size: int, S: int, I: int) -> int:
+    """Row alignment of the chunked-context workspace: the KV block size and,
+    under DCP (S > 1), also the S * I dealing unit, i.e. their least common
+    multiple.  prhub.com.cn summary of PR 50484, "implementation breakdown"
+    step 3 and the mla_attention.py excerpt of the workspace alignment."""
+    a = int(block_size)
+    if S > 1:
+        a = math.lcm(a, int(S) * int(I))
+    return a
+
+
+def align_chunked_context_workspace(workspace_rows: int, block_size: int, S: int, I: int,
+                                    max_num_seqs: int) -> int:
+    """Workspace rows after alignment: at least max_num_seqs aligned rows,
+    at least the requested size, rounded up to a multiple of the alignment
+    (same excerpt as above)."""
+    a = chunked_context_alignment(block_size, S, I)
+    ws = max(int(workspace_rows), int(max_num_seqs) * a)
+    return -(-ws // a) * a
+
+
+def context_chunk_plan(context_lens, workspace_rows: int, alignment: int):
+    """Split every request's cached context into chunks that fit the workspace.
+
+    Returns (C, starts [K, B], lens [K, B]) with K the number of chunks: chunk
+    k of request b starts at k * C and holds min(C, context_lens[b] - k * C)
+    rows (0 once the context is used up).  C == 0 and K == 0 when no request
+    has a context; C is None when the workspace cannot hold one aligned row
+    block per request with a context.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    n = int(np.count_nonzero(ctx > 0))
+    if n == 0:
+        return 0, np.zeros((0, ctx.size), np.int64), np.zeros((0, ctx.size), np.int64)
+    C = (int(workspace_rows) // (n * int(alignment))) * int(alignment)
+    if C == 0:
+        return None, None, None
+    K = -(-int(ctx.max()) // C)
+    starts = np.zeros((K, ctx.size), np.int64)
+    lens = np.zeros((K, ctx.size), np.int64)
+    for k in range(K):
+        starts[k] = k * C
+        lens[k] = np.clip(ctx - k * C, 0, C)
+    return C, starts, lens
+
+
+def gather_context_chunk_oracle(kv_bits, local_tables, chunk_starts, chunk_lens, S: int, I: int):
+    """Rows of one context chunk in global order, read from S shard-local caches.
+
+    kv_bits uint16 [num_blocks, block_size, 576] (bf16 bits: the pool holding
+    every shard's local blocks), local_tables int [S, B, max_blocks],
+    chunk_starts / chunk_lens int [B].  Returns uint16 [sum(chunk_lens), 576]:
+    for request b, global positions chunk_starts[b] .. + chunk_lens[b] - 1,
+    each taken from shard shard_of_token(t) at its local index.
+    """
+    kv_bits = np.asarray(kv_bits)
+    tables = np.asarray(local_tables, dtype=np.int64)
+    bs = kv_bits.shape[1]
+    rows = []
+    for b in range(tables.shape[1]):
+        t = np.arange(int(chunk_starts[b]), int(chunk_starts[b]) + int(chunk_lens[b]), dtype=np.int64)
+        s = shard_of_token(t, S, I)
+        j = local_index_of_token(t, S, I)
+        blk = tables[s, b, j // bs]
+        rows.append(kv_bits[blk, j % bs])
+    if not rows:
+        return np.zeros((0, kv_bits.shape[2]), kv_bits.dtype)
+    return np.concatenate(rows, axis=0)

@@ -404,3 +404,193 @@ def test_merge_states_far_apart_lses(gap):
             want = p[t, h] if strong_prefix else q[t, h]
             np.testing.assert_allclose(out[t, h], want, rtol=4e-16, atol=0)
             assert lse[h, t] == max(lp[h, t], ls[h, t])
+
+
+# --- chunked-context KV gather ------------------------------------------------
+
+def _dealt_local_caches(ctx_lens, S, I, bs, seed):
+    """Shard-local paged caches built without the oracle's formulas: each
+    request's tokens are dealt to the shards by ``_brute.deal_tokens`` and
+    appended to that shard's local list, which fills shuffled physical
+    blocks in order.  Columns 0-2 of a row hold (request, token low 16 bits,
+    token high bits); the other columns are random bits."""
+    rng = np.random.default_rng(seed)
+    B = len(ctx_lens)
+    local = [[[] for _ in range(B)] for _ in range(S)]
+    for b, n in enumerate(ctx_lens):
+        for t, s in enumerate(_brute.deal_tokens(n, S, I)):
+            local[s][b].append(t)
+    need = [[-(-len(local[s][b]) // bs) for b in range(B)] for s in range(S)]
+    maxb = max(1, max(max(row) for row in need))
+    total = sum(sum(row) for row in need)
+    perm = iter(rng.permutation(np.arange(1, total + 1)))
+    kv = rng.integers(0, 1 << 16, size=(total + 1, bs, mla_oracle.D_QK), dtype=np.uint16)
+    tables = np.zeros((S, B, maxb), np.int32)
+    for s in range(S):
+        for b in range(B):
+            for i in range(need[s][b]):
+                blk = int(next(perm))
+                tables[s, b, i] = blk
+                for slot, t in enumerate(local[s][b][i * bs:(i + 1) * bs]):
+                    kv[blk, slot, 0] = b
+                    kv[blk, slot, 1] = t & 0xFFFF
+                    kv[blk, slot, 2] = t >> 16
+    return kv, tables
+
+
+GATHER_CASES = [  # S, I, block_size, context lengths
+    (1, 1, 16, [0, 5, 40]),
+    (2, 1, 1, [7, 0, 33]),
+    (3, 2, 4, [1, 50, 19]),
+    (8, 1, 64, [300, 1, 0, 129]),
+    (8, 16, 64, [1000, 17]),
+    (5, 3, 8, [222, 89, 3]),
+    (4, 64, 16, [70000]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GATHER_CASES)))
+def test_gather_context_chunk_against_dealt_caches(case):
+    """Every gathered row is the request's own token, in global order, for
+    random chunk windows (whole contexts, empty windows, ragged tails)."""
+    S, I, bs, ctx = GATHER_CASES[case]
+    kv, tables = _dealt_local_caches(ctx, S, I, bs, seed=case)
+    rng = np.random.default_rng(100 + case)
+    for trial in range(6):
+        starts, lens = [], []
+        for n in ctx:
+            a = int(rng.integers(0, n + 1)) if trial else 0
+            e = n if trial < 2 else int(rng.integers(a, n + 1))
+            starts.append(a)
+            lens.append(e - a)
+        rows = mla_oracle.gather_context_chunk_oracle(kv, tables, starts, lens, S, I)
+        want = [(b, t) for b in range(len(ctx)) for t in range(starts[b], starts[b] + lens[b])]
+        assert rows.shape == (len(want), mla_oracle.D_QK)
+        got = [(int(r[0]), int(r[1]) | (int(r[2]) << 16)) for r in rows]
+        assert got == want
+
+
+def _brute_lcm_alignment(bs, S, I):
+    m = 1
+    while m % bs or (S > 1 and m % (S * I)):
+        m += 1
+    return m
+
+
+def test_chunked_context_alignment_values():
+    """Closed forms (lcm of the block size and S * I under DCP), then brute
+    search for the least row count both divide."""
+    assert mla_oracle.chunked_context_alignment(64, 1, 1) == 64
+    assert mla_oracle.chunked_context_alignment(64, 1, 16) == 64   # no DCP: block size only
+    assert mla_oracle.chunked_context_alignment(64, 8, 1) == 64
+    assert mla_oracle.chunked_context_alignment(64, 8, 16) == 128
+    assert mla_oracle.chunked_context_alignment(64, 3, 1) == 192
+    assert mla_oracle.chunked_context_alignment(16, 8, 3) == 48
+    for bs in (1, 2, 16, 48, 64):
+        for S in (1, 2, 3, 8):
+            for I in (1, 2, 3, 16):
+                assert mla_oracle.chunked_context_alignment(bs, S, I) == _brute_lcm_alignment(bs, S, I)
+
+
+def test_aligned_workspace_is_the_least_valid_size():
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        bs = int(rng.choice([1, 16, 64, 128]))
+        S = int(rng.integers(1, 9))
+        I = int(rng.choice([1, 2, 16]))
+        mns = int(rng.integers(1, 300))
+        ws = int(rng.integers(0, 1 << 18))
+        a = _brute_lcm_alignment(bs, S, I)
+        got = mla_oracle.align_chunked_context_workspace(ws, bs, S, I, mns)
+        floor = max(ws, mns * a)
+        assert got % a == 0 and got >= floor and got - a < floor
+
+
+def test_context_chunk_plan_covers_each_token_once():
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        B = int(rng.integers(1, 9))
+        ctx = rng.integers(0, 5000, size=B)
+        if trial % 5 == 0:
+            ctx[rng.integers(0, B)] = 0
+        a = int(rng.choice([1, 16, 64, 192]))
+        ws = int(rng.integers(0, 40000))
+        C, starts, lens = mla_oracle.context_chunk_plan(ctx, ws, a)
+        n = int(np.count_nonzero(ctx))
+        if n == 0:
+            assert C == 0 and starts.shape[0] == 0
+            continue
+        if ws < n * a:
+            assert C is None
+            continue
+        assert C % a == 0 and n * C <= ws < n * (C + a)     # the largest aligned chunk
+        assert np.all(starts % a == 0)
+        assert np.all(lens.sum(axis=1) <= ws)               # every chunk fits the workspace
+        for b in range(B):
+            covered = []
+            for k in range(starts.shape[0]):
+                covered.extend(range(int(starts[k, b]), int(starts[k, b] + lens[k, b])))
+            assert covered == list(range(int(ctx[b])))
+
+
+def test_aligned_chunks_take_one_contiguous_local_run_per_shard():
+    """What the S * I alignment buys: a chunk that starts on a multiple of
+    S * I takes from every shard one contiguous run of local rows starting
+    at start / S, of equal length when the chunk is a multiple of S * I long
+    (local order found by dealing, not by the oracle's formula)."""
+    for S, I in [(2, 1), (8, 1), (8, 16), (3, 5)]:
+        n = 40 * S * I + 7
+        owner = _brute.deal_tokens(n, S, I)
+        local_pos = {}
+        seen = [0] * S
+        for t, s in enumerate(owner):
+            local_pos[t] = seen[s]
+            seen[s] += 1
+        for start in range(0, n, S * I):
+            for L in (S * I, 3 * S * I, n - start):
+                L = min(L, n - start)
+                for s in range(S):
+                    js = [local_pos[t] for t in range(start, start + L) if owner[t] == s]
+                    assert js == list(range(start // S, start // S + len(js)))
+                    assert [mla_oracle.local_index_of_token(t, S, I)
+                            for t in range(start, start + L) if owner[t] == s] == js
+                    if L % (S * I) == 0:
+                        assert len(js) == L // S
+
+
+@pytest.mark.parametrize("mutation", ["local_no_interleave", "local_no_offset", "shard_mod_s",
+                                      "alignment_block_only", "plan_divides_by_batch"])
+def test_planted_gather_mistakes_are_caught(monkeypatch, mutation):
+    """Each plausible bug in the gather's oracle, planted on the CPU, fails a pin."""
+    if mutation == "local_no_interleave":
+        monkeypatch.setattr(mla_oracle, "local_index_of_token", lambda t, S, I: t // S)
+    elif mutation == "local_no_offset":
+        monkeypatch.setattr(mla_oracle, "local_index_of_token", lambda t, S, I: (t // (S * I)) * I)
+    elif mutation == "shard_mod_s":
+        monkeypatch.setattr(mla_oracle, "shard_of_token", lambda t, S, I: t % S)
+    elif mutation == "alignment_block_only":
+        monkeypatch.setattr(mla_oracle, "chunked_context_alignment", lambda bs, S, I: bs)
+    else:
+        def by_batch(ctx, ws, a):  # shares the workspace among all requests, not those with a context
+            ctx = np.asarray(ctx, dtype=np.int64)
+            if not np.any(ctx > 0):
+                return 0, np.zeros((0, ctx.size), np.int64), np.zeros((0, ctx.size), np.int64)
+            C = (ws // (ctx.size * a)) * a
+            if C == 0:
+                return None, None, None
+            K = -(-int(ctx.max()) // C)
+            starts = np.array([[k * C] * ctx.size for k in range(K)], np.int64)
+            return C, starts, np.clip(ctx[None, :] - starts, 0, C)
+        monkeypatch.setattr(mla_oracle, "context_chunk_plan", by_batch)
+    tests = [lambda: [test_gather_context_chunk_against_dealt_caches(c) for c in range(len(GATHER_CASES))],
+             test_chunked_context_alignment_values, test_aligned_workspace_is_the_least_valid_size,
+             test_context_chunk_plan_covers_each_token_once,
+             test_aligned_chunks_take_one_contiguous_local_run_per_shard]
+    caught = False
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            caught = True
+            break
+    assert caught, mutation
