@@ -59,6 +59,8 @@ def parse():
                          "HBM-fed step's)")
     ap.add_argument("--no-merge", action="store_true",
                     help="skip the timing of the two-way prefix/suffix merge")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the timing of the chunked-context KV gather")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -215,21 +217,69 @@ def merge_leg(mla, dev, launches):
     s = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
     lp = torch.rand((MERGE_H, MERGE_T), generator=gen, device=dev) * 15 - 3
     ls = torch.rand((MERGE_H, MERGE_T), generator=gen, device=dev) * 15 - 3
-    ms = []
-    for i in range(launches):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+    for _ in range(2):
         mla.mla_merge_states(p, lp, s, ls, out=p, out_lse=lp)
-        e1.record()
-        torch.cuda.synchronize()
-        if i >= 2:
-            ms.append(e0.elapsed_time(e1))
+    torch.cuda.synchronize()
+    # back-to-back launches between two events, so that the host's own time
+    # per launch is hidden behind the kernels
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        mla.mla_merge_states(p, lp, s, ls, out=p, out_lse=lp)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
     rows = MERGE_T * MERGE_H
     nbytes = 3 * rows * MERGE_D * 2 + 3 * rows * 4
-    med = statistics.median(ms)
-    gbps = nbytes / (med / 1e3) / 1e9
+    gbps = nbytes / (ms / 1e3) / 1e9
     return {"kernel": "mla::merge_kernel<1>", "workload": f"T={MERGE_T} H={MERGE_H} D={MERGE_D} bf16, in place",
-            "ms": med, "bytes_per_launch": nbytes, "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+            "ms": ms, "launches_timed": launches, "bytes_per_launch": nbytes, "achieved_gbps": gbps,
+            "frac": gbps / HBM_PEAK_GBPS}
+
+
+def gather_leg(mla, dev, steps):
+    """Time the chunked-context KV gather of the 120k-token run's cached
+    context: one step gathers every chunk of the plan (each request's whole
+    context once); per row it reads 1152 bytes of KV and writes 1152."""
+    import torch
+    import workloads
+    w = workloads.long_context_gather()
+    kv = torch.from_numpy(w.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    tables = torch.from_numpy(w.local_tables).to(dev)
+    align = mla.mla_chunked_context_alignment(w.block_size, w.num_shards, w.interleave)
+    ws_rows = mla.mla_align_chunked_context_workspace(w.workspace_rows, w.block_size, w.num_shards,
+                                                      w.interleave, len(w.context_lens))
+    C, K, _, _ = mla.mla_context_chunk_plan(w.context_lens, ws_rows, align)
+    chunks = []
+    for k in range(K):
+        _, _, st, cu = mla.mla_context_chunk_plan(w.context_lens, ws_rows, align, chunk_index=k)
+        chunks.append((torch.from_numpy(st).to(dev), torch.from_numpy(cu).to(dev), int(cu[-1])))
+    out = torch.empty((ws_rows, 576), dtype=torch.bfloat16, device=dev)
+    rows = sum(c[2] for c in chunks)
+    views = [(st, cu, out[:n]) for st, cu, n in chunks]
+
+    def one_step():
+        for st, cu, o in views:
+            mla.mla_gather_context_chunk(kv, tables, st, cu, w.interleave, out=o)
+
+    for _ in range(2):
+        one_step()
+    torch.cuda.synchronize()
+    # back-to-back steps between two events (the host's time per launch hidden)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one_step()
+    e1.record()
+    torch.cuda.synchronize()
+    med = e0.elapsed_time(e1) / steps
+    nbytes = 2 * rows * ROW_BYTES
+    gbps = nbytes / (med / 1e3) / 1e9
+    return {"kernel": "mla::gather_kernel", "workload": w.name, "chunks": K, "chunk_rows": C,
+            "alignment": align, "workspace_rows": ws_rows, "rows_per_step": rows, "steps_timed": steps,
+            "ms_per_step": med,
+            "bytes_per_step": nbytes, "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "rows_per_s": rows / (med / 1e3)}
 
 
 def pct(xs, q):
@@ -336,6 +386,8 @@ def main():
 
     # the two-way prefix/suffix merge, in place, on a chunked-context shape
     merge = None if args.no_merge else merge_leg(mla, dev, args.event_steps + 2)
+    # the chunked-context KV gather (the prefill side of the same shards)
+    gather = None if args.no_gather else gather_leg(mla, dev, args.event_steps)
 
     # K steps in one graph, replayed between synchronisations
     K = args.steps
@@ -397,6 +449,8 @@ def main():
     }
     if merge is not None:
         rec["merge_states"] = merge
+    if gather is not None:
+        rec["context_gather"] = gather
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -71,8 +71,11 @@ enum { MLA_HEAD_DIM = 576, MLA_V_DIM = 512 };
 enum {
   MLA_FAULT_BLOCK_ID = 1, /* a referenced block_table entry outside [0, num_blocks)      */
   MLA_FAULT_SEQ_LEN = 2,  /* seq_lens[b] < 0 or > max_blocks_per_seq * block_size       */
-  MLA_FAULT_PLAN = 4      /* the device work plan did not fit the workspace (never with a */
+  MLA_FAULT_PLAN = 4,     /* the device work plan did not fit the workspace (never with a */
                           /* workspace of mla_workspace_bytes(a) bytes)                  */
+  MLA_FAULT_CHUNK = 8     /* gather: cu_rows not non-decreasing from 0 up to at most     */
+                          /* out_rows, a negative chunk start, or a local position past  */
+                          /* the block table's width                                     */
 };
 
 typedef struct mla_decode_args {
@@ -184,11 +187,95 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
                            void* ev_mid, void* ev_end);
 
 /* The fault word (MLA_FAULT_* bits) of the last decode call enqueued on
- * `stream` with `workspace`: waits for the stream, then copies the word to
- * *faults.  0 means the call met no device-detected fault.  This is the one
+ * `stream` with `workspace` (or, given a gather's `faults` pointer, that
+ * word): waits for the stream, then copies the word to *faults.  0 means the call met no device-detected fault.  This is the one
  * call that synchronises.  Errors: MLA_ERR_INVALID_ARG (null pointer),
  * MLA_ERR_HIP. */
 int mla_device_faults(const void* workspace, void* stream, int32_t* faults);
+
+/* ------------------------------------------------------------------------
+ * Chunked-context KV gather (the prefill side of DCP).
+ *
+ * A prefill whose request has a cached context attends to it chunk by chunk,
+ * each chunk's KV rows first gathered into a contiguous workspace in global
+ * token order.  Under DCP every shard keeps only its share of the context in
+ * its own paged cache, so the gather reassembles each chunk from the S
+ * shard-local caches (vLLM PR 50484 page, "Summary": the chunked-context KV
+ * gather; its prhub.com.cn summary, "implementation breakdown" step 2, the
+ * chunked-context prefill routed through the KV gather, and step 3, the
+ * workspace aligned to lcm(block_size, dcp_size * interleave)).  Shard s's
+ * local token j is the j-th token the round-robin deal gives it, stored at
+ * slot j % block_size of block block_tables[s][b][j / block_size]; on one
+ * device the S shards' local blocks share one pool of physical blocks.
+ * Workspace sizes count rows of 576 bf16 values (one row per token).
+ * ------------------------------------------------------------------------ */
+
+typedef struct mla_gather_args {
+  const void* kv_cache;         /* device bf16 [num_blocks, block_size, 576]: the pool of   */
+                                /* every shard's local blocks                               */
+  const int32_t* block_tables;  /* device int32 [S, B, max_blocks_per_seq]: local block ids */
+  const int32_t* chunk_starts;  /* device int32 [B]: global position of request b's first   */
+                                /* chunk row                                                */
+  const int32_t* cu_rows;       /* device int32 [B + 1]: request b's rows are workspace     */
+                                /* rows [cu_rows[b], cu_rows[b + 1]); cu_rows[0] == 0       */
+  int32_t batch;                /* B >= 0 (<= 2^24); B == 0 enqueues nothing                */
+  int32_t num_blocks;           /* physical blocks in kv_cache, >= 1                        */
+  int32_t block_size;           /* a power of two, 1..1024                                  */
+  int32_t max_blocks_per_seq;   /* width of each shard's table, >= 1                        */
+  int32_t num_shards;           /* S >= 1, S * I <= 2^24                                    */
+  int32_t interleave;           /* I >= 1: global token t lives on shard (t / I) % S        */
+} mla_gather_args;
+
+/* Row alignment of the chunked-context workspace: block_size, and with
+ * num_shards > 1 lcm(block_size, num_shards * interleave) (prhub.com.cn
+ * summary of PR 50484, "implementation breakdown" step 3, and its
+ * mla_attention.py excerpt of the alignment).  -1 for a non-positive
+ * argument. */
+int64_t mla_chunked_context_alignment(int32_t block_size, int32_t num_shards, int32_t interleave);
+
+/* Workspace rows after alignment (same source): max(workspace_rows,
+ * max_num_seqs * alignment) rounded up to a multiple of the alignment.  -1
+ * for a negative size, a non-positive block_size / num_shards / interleave,
+ * or a result that would overflow. */
+int64_t mla_align_chunked_context_workspace(int64_t workspace_rows, int32_t block_size,
+                                            int32_t num_shards, int32_t interleave,
+                                            int32_t max_num_seqs);
+
+/* Host-side chunk plan (host pointers only; enqueues nothing).  The pages fix
+ * the alignment but not the split, so this takes the plain reading: every
+ * request's chunk length is the same C, the largest multiple of `alignment`
+ * with n * C <= workspace_rows, n the number of requests with a nonzero
+ * context; chunk k of request b covers context positions [k C, min((k + 1) C,
+ * context_lens[b])).  Writes *chunk_tokens = C and *num_chunks = K (both 0
+ * when no request has a context).  When chunk_starts (int32 [batch]) or
+ * cu_rows (int32 [batch + 1]) is non-NULL, also writes chunk chunk_index's
+ * starts (k C) and packed row offsets, ready for mla_gather_context_chunk.
+ * Errors: MLA_ERR_INVALID_ARG (null context_lens or outputs, a negative
+ * length, alignment < 1, workspace_rows outside [0, 2^31), chunk_index
+ * outside [0, K) when metadata is asked for), MLA_ERR_WORKSPACE_TOO_SMALL
+ * (the workspace cannot hold one aligned block per request with a
+ * context). */
+int mla_context_chunk_plan(const int32_t* context_lens, int32_t batch, int64_t workspace_rows,
+                           int64_t alignment, int32_t chunk_index, int32_t* chunk_tokens,
+                           int32_t* num_chunks, int32_t* chunk_starts, int32_t* cu_rows);
+
+/* Gather one context chunk into `out` (device bf16 [out_rows, 576], 16-byte
+ * aligned, caller-owned): workspace row cu_rows[b] + i is request b's global
+ * token chunk_starts[b] + i, read from shard (t / I) % S at local index
+ * (t / (S I)) I + t % I.  Rows [cu_rows[B], out_rows) are left untouched.
+ * Launch geometry depends on out_rows only.  Device-detected faults (a
+ * referenced table entry outside [0, num_blocks), a negative chunk start, a
+ * local position past the table's width, cu_rows[B] outside [0, out_rows])
+ * fill the affected rows with bf16 NaN (every row in the last case) and OR
+ * MLA_FAULT_BLOCK_ID / MLA_FAULT_CHUNK into *faults (device int32, may be
+ * NULL; zeroed by the caller; readable with mla_device_faults).  cu_rows
+ * that do not start at 0 or that decrease set MLA_FAULT_CHUNK too; the
+ * rows are then unspecified (but nothing outside `out` is written).
+ * Errors: MLA_ERR_INVALID_ARG (null or misaligned pointers, negative sizes,
+ * out_rows >= 2^31 - 64), MLA_ERR_UNSUPPORTED (block_size not a power of two
+ * up to 1024, S * I or B above 2^24), MLA_ERR_HIP. */
+int mla_gather_context_chunk(const mla_gather_args* a, void* out, int32_t out_rows, int32_t* faults,
+                             void* stream);
 
 /* A static string naming a status code. */
 const char* mla_status_string(int status);

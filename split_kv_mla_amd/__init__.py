@@ -9,8 +9,13 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     MlaDecodeArgs,
     MlaError,
+    MlaGatherArgs,
     decode_args,
     load_library,
+    mla_align_chunked_context_workspace,
+    mla_chunked_context_alignment,
+    mla_context_chunk_plan,
+    mla_gather_context_chunk,
     mla_device_faults,
     mla_lse_combine,
     mla_merge_states,

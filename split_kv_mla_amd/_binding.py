@@ -40,6 +40,21 @@ class MlaDecodeArgs(ctypes.Structure):
     ]
 
 
+class MlaGatherArgs(ctypes.Structure):
+    _fields_ = [
+        ("kv_cache", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("chunk_starts", ctypes.c_void_p),
+        ("cu_rows", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_shards", ctypes.c_int32),
+        ("interleave", ctypes.c_int32),
+    ]
+
+
 class MlaError(RuntimeError):
     pass
 
@@ -79,6 +94,16 @@ def load_library(path: str = LIB_PATH):
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_device_faults.argtypes = [ctypes.c_void_p, ctypes.c_void_p, P(ctypes.c_int32)]
     lib.mla_device_faults.restype = ctypes.c_int
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.mla_chunked_context_alignment.argtypes = [i32, i32, i32]
+    lib.mla_chunked_context_alignment.restype = i64
+    lib.mla_align_chunked_context_workspace.argtypes = [i64, i32, i32, i32, i32]
+    lib.mla_align_chunked_context_workspace.restype = i64
+    lib.mla_context_chunk_plan.argtypes = [P(i32), i32, i64, i64, i32, P(i32), P(i32), P(i32), P(i32)]
+    lib.mla_context_chunk_plan.restype = ctypes.c_int
+    lib.mla_gather_context_chunk.argtypes = [P(MlaGatherArgs), ctypes.c_void_p, i32, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    lib.mla_gather_context_chunk.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -151,13 +176,17 @@ def mla_plan_capacity(args: MlaDecodeArgs, shard_count=None):
     return int(n), int(rg.value)
 
 
-FAULT_BLOCK_ID, FAULT_SEQ_LEN, FAULT_PLAN = 1, 2, 4
+FAULT_BLOCK_ID, FAULT_SEQ_LEN, FAULT_PLAN, FAULT_CHUNK = 1, 2, 4, 8
 
 
 def mla_device_faults(workspace) -> int:
     """Fault word (FAULT_* bits) of the last decode call that used `workspace`
-    on the current stream; waits for that stream."""
-    _need(workspace, "workspace", torch.uint8)
+    (uint8), or the int32 fault word given to a gather, on the current
+    stream; waits for that stream."""
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype not in (torch.uint8, torch.int32):
+        raise TypeError("workspace must be a uint8 workspace or an int32 fault word")
+    if workspace.numel() * workspace.element_size() < 4:
+        raise ValueError("the fault word needs 4 bytes")
     f = ctypes.c_int32(-1)
     _check(load_library().mla_device_faults(_ptr(workspace), _stream(workspace.device), ctypes.byref(f)))
     return int(f.value)
@@ -299,3 +328,82 @@ def mla_merge_states(prefix, prefix_lse, suffix, suffix_lse, out=None, out_lse=N
         _ptr(out), _ptr(out_lse), o_sh, o_st, _ptr(prefix), _ptr(prefix_lse), p_sh, p_st,
         _ptr(suffix), _ptr(suffix_lse), s_sh, s_st, T, H, D, _MERGE_DTYPES[prefix.dtype], _stream(dev)))
     return out, out_lse
+
+
+# --- chunked-context KV gather ------------------------------------------------
+
+def mla_chunked_context_alignment(block_size, num_shards, interleave) -> int:
+    """Row alignment of the chunked-context workspace (lcm(block, S * I) under DCP)."""
+    a = int(load_library().mla_chunked_context_alignment(block_size, num_shards, interleave))
+    if a < 1:
+        raise MlaError("invalid alignment arguments")
+    return a
+
+
+def mla_align_chunked_context_workspace(workspace_rows, block_size, num_shards, interleave, max_num_seqs) -> int:
+    """Workspace rows rounded up to the alignment, at least max_num_seqs aligned rows."""
+    n = int(load_library().mla_align_chunked_context_workspace(workspace_rows, block_size, num_shards,
+                                                              interleave, max_num_seqs))
+    if n < 0:
+        raise MlaError("invalid workspace alignment arguments")
+    return n
+
+
+def mla_context_chunk_plan(context_lens, workspace_rows, alignment, chunk_index=None):
+    """Chunk length C and chunk count K for host context lengths; with
+    ``chunk_index``, also that chunk's int32 starts [B] and row offsets
+    [B + 1] (host numpy arrays).  Returns (C, K, starts, cu_rows)."""
+    import numpy as np
+    ctx = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    B = ctx.size
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    C, K = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    starts = cu = None
+    if chunk_index is not None:
+        starts = np.zeros(max(B, 1), np.int32)
+        cu = np.zeros(B + 1, np.int32)
+    _check(load_library().mla_context_chunk_plan(
+        ctx.ctypes.data_as(i32p), B, int(workspace_rows), int(alignment),
+        -1 if chunk_index is None else int(chunk_index), ctypes.byref(C), ctypes.byref(K),
+        None if starts is None else starts.ctypes.data_as(i32p),
+        None if cu is None else cu.ctypes.data_as(i32p)))
+    return int(C.value), int(K.value), (None if starts is None else starts[:B]), cu
+
+
+def mla_gather_context_chunk(kv_cache, block_tables, chunk_starts, cu_rows, interleave, out=None,
+                             out_rows=None, faults=None):
+    """Gather one context chunk from S shard-local caches into global order.
+
+    kv_cache bf16 [num_blocks, block_size, 576]; block_tables int32 [S, B,
+    max_blocks]; chunk_starts int32 [B]; cu_rows int32 [B + 1]; out bf16
+    [out_rows, 576] (allocated when None: give ``out_rows`` = cu_rows[B]);
+    faults: an int32 tensor whose first element the kernel ORs fault bits
+    into (zero it first).  Returns out.
+    """
+    dev = kv_cache.device
+    if kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM:
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
+    _need(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    if block_tables.dim() != 3:
+        raise ValueError("block_tables must be [S, B, max_blocks_per_seq]")
+    S, B, maxb = block_tables.shape
+    _need(block_tables, "block_tables", torch.int32, device=dev)
+    _need(chunk_starts, "chunk_starts", torch.int32, (B,), dev)
+    _need(cu_rows, "cu_rows", torch.int32, (B + 1,), dev)
+    if out is None:
+        if out_rows is None:
+            raise ValueError("give out or out_rows")
+        out = torch.empty((int(out_rows), HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    if out.dim() != 2 or out.shape[1] != HEAD_DIM:
+        raise ValueError("out must be [rows, 576]")
+    _need(out, "out", torch.bfloat16, device=dev)
+    if faults is not None:
+        _need(faults, "faults", torch.int32, device=dev)
+    a = MlaGatherArgs()
+    a.kv_cache, a.block_tables = kv_cache.data_ptr(), block_tables.data_ptr()
+    a.chunk_starts, a.cu_rows = chunk_starts.data_ptr(), cu_rows.data_ptr()
+    a.batch, a.num_blocks, a.block_size = B, kv_cache.shape[0], kv_cache.shape[1]
+    a.max_blocks_per_seq, a.num_shards, a.interleave = maxb, S, int(interleave)
+    _check(load_library().mla_gather_context_chunk(ctypes.byref(a), _ptr(out), out.shape[0], _ptr(faults),
+                                                   _stream(dev)))
+    return out

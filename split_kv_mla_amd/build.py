@@ -8,8 +8,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_split_kv.so")
-SOURCES = [os.path.join(HERE, "csrc", "mla_split_kv.hip"), os.path.join(HERE, "csrc", "mla_merge.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "mla_split_kv.hip"), os.path.join(HERE, "csrc", "mla_merge.hip"),
+           os.path.join(HERE, "csrc", "mla_gather.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "mla_kernels.h"), os.path.join(HERE, "csrc", "mla_plan.h"),
+           os.path.join(HERE, "csrc", "mla_merge.h"), os.path.join(HERE, "csrc", "mla_gather.h"),
            os.path.join(ROOT, "include", "mla_split_kv.h")]
 
 

@@ -272,3 +272,85 @@ def test_workspace_opens_with_the_fault_word_header():
     body = 256 * (-(-4 * (a.batch * a.num_shards + 2) // 256)) + 256 * (-(-4 * items * rows // 256)) \
         + 256 * (-(-items * rows // 256)) + 256 * (-(-4 * items * rows * 512 // 256))
     assert m.mla_workspace_bytes(a) == 256 + body
+
+
+# --- chunked-context KV gather: host-side sizing, plan and argument checks ------
+
+def test_chunked_context_host_helpers_match_the_oracle():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        bs = int(rng.choice([1, 16, 64, 256]))
+        S = int(rng.integers(1, 17))
+        I = int(rng.choice([1, 2, 3, 16, 64]))
+        mns = int(rng.integers(0, 1024))
+        ws = int(rng.integers(0, 1 << 20))
+        assert m.mla_chunked_context_alignment(bs, S, I) == oracle.chunked_context_alignment(bs, S, I)
+        assert m.mla_align_chunked_context_workspace(ws, bs, S, I, mns) == \
+            oracle.align_chunked_context_workspace(ws, bs, S, I, mns)
+    for _ in range(300):
+        B = int(rng.integers(1, 20))
+        ctx = rng.integers(0, 200000, size=B)
+        ctx[rng.random(B) < 0.2] = 0
+        a = int(rng.choice([16, 64, 128, 192]))
+        ws = int(rng.integers(1, 1 << 18))
+        C, starts, lens = oracle.context_chunk_plan(ctx, ws, a)
+        if C is None:
+            with pytest.raises(m.MlaError):
+                m.mla_context_chunk_plan(ctx, ws, a)
+            continue
+        c, k, _, _ = m.mla_context_chunk_plan(ctx, ws, a)
+        assert (c, k) == (C, starts.shape[0])
+        for ki in range(k):
+            c, k2, st, cu = m.mla_context_chunk_plan(ctx, ws, a, chunk_index=ki)
+            assert st.tolist() == starts[ki].tolist()
+            assert cu.tolist() == [0] + np.cumsum(lens[ki]).tolist()
+
+
+def test_chunk_plan_rejects_bad_arguments():
+    lib = m.load_library()
+    i32 = ctypes.c_int32
+    ctx = (i32 * 2)(100, 50)
+    C, K = i32(), i32()
+    st, cu = (i32 * 2)(), (i32 * 3)()
+    assert lib.mla_context_chunk_plan(ctx, 2, 1000, 64, 0, ctypes.byref(C), ctypes.byref(K), st, cu) == 0
+    assert (C.value, K.value, list(cu)) == (448, 1, [0, 100, 150])
+    assert lib.mla_context_chunk_plan(ctx, 2, 100, 64, 0, ctypes.byref(C), ctypes.byref(K), st, cu) == -3
+    assert lib.mla_context_chunk_plan(ctx, 2, 1000, 0, 0, ctypes.byref(C), ctypes.byref(K), st, cu) == -1
+    assert lib.mla_context_chunk_plan(ctx, 2, 1 << 31, 64, 0, ctypes.byref(C), ctypes.byref(K), st, cu) == -1
+    assert lib.mla_context_chunk_plan(ctx, 2, 1000, 64, 1, ctypes.byref(C), ctypes.byref(K), st, cu) == -1
+    assert lib.mla_context_chunk_plan(None, 2, 1000, 64, 0, ctypes.byref(C), ctypes.byref(K), st, cu) == -1
+    neg = (i32 * 2)(100, -1)
+    assert lib.mla_context_chunk_plan(neg, 2, 1000, 64, 0, ctypes.byref(C), ctypes.byref(K), None, None) == -1
+    zero = (i32 * 2)(0, 0)
+    assert lib.mla_context_chunk_plan(zero, 2, 0, 64, -1, ctypes.byref(C), ctypes.byref(K), None, None) == 0
+    assert (C.value, K.value) == (0, 0)
+
+
+def _gather_args(B=2, S=8, I=1, bs=64, maxb=16, nb=100):
+    a = _binding.MlaGatherArgs()
+    a.kv_cache = a.block_tables = a.chunk_starts = a.cu_rows = 0x1000  # never dereferenced here
+    a.batch, a.num_blocks, a.block_size, a.max_blocks_per_seq = B, nb, bs, maxb
+    a.num_shards, a.interleave = S, I
+    return a
+
+
+def test_gather_rejects_bad_arguments_without_launching():
+    lib = m.load_library()
+    vp = ctypes.c_void_p
+    good = vp(0x2000)
+
+    def call(out=good, rows=64, **kw):
+        return lib.mla_gather_context_chunk(ctypes.byref(_gather_args(**kw)), out, rows, None, vp(0))
+
+    assert call(rows=0) == 0 and call(B=0) == 0          # nothing to do, nothing launched
+    assert call(out=vp(0)) == -1 and call(rows=-1) == -1
+    assert call(out=vp(0x2008)) == -1                    # misaligned output
+    assert call(S=0) == -1 and call(I=0) == -1 and call(nb=0) == -1 and call(maxb=0) == -1
+    assert call(B=-1) == -1 and call(rows=(1 << 31) - 1) == -1
+    assert call(bs=48) == -2 and call(bs=2048) == -2     # block size not a power of two up to 1024
+    assert call(S=4097, I=4096) == -2                    # S * I above 2^24
+    a = _gather_args()
+    a.cu_rows = 0
+    assert lib.mla_gather_context_chunk(ctypes.byref(a), good, 64, None, vp(0)) == -1

@@ -10,5 +10,8 @@ from .gen import (  # noqa: F401
     verify,
     padded,
     merge_inputs,
+    GatherWorkload,
+    context_gather,
+    long_context_gather,
     STANDARD,
 )

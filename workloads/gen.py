@@ -260,3 +260,70 @@ def merge_inputs(T, H, D, dtype, seed, empty_frac=0.1, both_empty_frac=0.02, gap
     p[np.isneginf(lp).T] = np.nan
     s[np.isneginf(ls).T] = np.nan
     return {"prefix": p, "prefix_lse": lp, "suffix": s, "suffix_lse": ls}
+
+
+# ---------------------------------------------------------------------------
+# Shard-local caches for the chunked-context KV gather.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class GatherWorkload:
+    name: str
+    kv_bits: np.ndarray         # uint16 [num_blocks, block_size, 576]: every shard's local blocks
+    local_tables: np.ndarray    # int32 [S, B, max_blocks]
+    context_lens: np.ndarray    # int32 [B]
+    num_shards: int
+    interleave: int
+    workspace_rows: int         # chunked-context workspace, in rows
+
+    @property
+    def block_size(self):
+        return self.kv_bits.shape[1]
+
+    def describe(self):
+        return {"workload": self.name, "batch": int(self.context_lens.size),
+                "context_lens": [int(x) for x in self.context_lens[:8]],
+                "block_size": int(self.block_size), "num_blocks": int(self.kv_bits.shape[0]),
+                "num_shards": self.num_shards, "interleave": self.interleave,
+                "workspace_rows": int(self.workspace_rows)}
+
+
+def context_gather(name, context_lens, num_shards, interleave, *, seed, block_size=64,
+                   workspace_rows=131072):
+    """Paged caches of S shards holding the requests' cached contexts.
+
+    Each shard gets, per request, enough blocks for any shard's share of the
+    context: at most ceil(L / (S I)) interleave units of I tokens.  Physical
+    blocks are a seeded permutation of 1..N; block 0 is a NaN poison block
+    that every unused table entry points at; cache values are N(0, 1)
+    rounded to bf16.
+    """
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    S, I = int(num_shards), int(interleave)
+    B = ctx.size
+    per = np.array([-(-(-(-int(n) // (S * I)) * I) // block_size) for n in ctx], dtype=np.int64)
+    max_blocks = max(1, int(per.max()) if B else 1)
+    total = int(per.sum()) * S
+    perm = rng.permutation(np.arange(1, total + 1, dtype=np.int64))
+    tables = np.zeros((S, B, max_blocks), dtype=np.int32)
+    k = 0
+    for s in range(S):
+        for b in range(B):
+            tables[s, b, :per[b]] = perm[k:k + per[b]]
+            k += per[b]
+    kv = np.empty((total + 1, block_size, ROW), dtype=np.uint16)
+    kv[0] = BF16_NAN
+    if total:
+        kv[1:] = _fill_normal(rng, (total, block_size, ROW))
+    return GatherWorkload(name=name, kv_bits=kv, local_tables=tables, context_lens=ctx.astype(np.int32),
+                          num_shards=S, interleave=I, workspace_rows=int(workspace_rows))
+
+
+def long_context_gather(seed=11):
+    """The chunked-context side of the 120k-token run: two requests whose
+    114000 cached context tokens (the shared prefix) are dealt over 8 shards,
+    each request's context stored in its own blocks, gathered through a
+    131072-row workspace."""
+    return context_gather("ctx_gather_b2_ctx114000_s8", [114000, 114000], 8, 1, seed=seed,
+                          workspace_rows=131072)
