@@ -12,6 +12,8 @@ from .mla_oracle import (  # noqa: F401
     D_QK,
     D_V,
     bf16_bits_to_f64,
+    fp8_e4m3_to_f64,
+    kv_rows_to_f64,
     row_length,
     shard_of_token,
     shard_token_sets,

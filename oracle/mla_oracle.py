@@ -50,6 +50,14 @@ and partial outputs, the same definition restricted to each shard's token
 set.  ``lse_combine_oracle`` is the textbook LSE-weighted merge, used for the
 standalone combine entry point and for the split-then-merge invariant.
 
+* An fp8 KV cache: the pages run verification plans on fp8 KV ("perf(mla):
+  fuse K3 DCP verification queries", PR 565 page, the dense-MLA metadata
+  review-fix commit text) and name the fp8_ds_mla cache format ("[Attention]
+  [MLA] FlashMLA sparse: DCP on the fp8_ds_mla mixed-batch path" page) but
+  define no row layout.  Reading taken here: every 576-wide row is stored as
+  576 fp8 E4M3 codes (OCP "fn" encoding) with one float32 scale per token;
+  the row's values are the codes' exact values times that scale.
+
 Readings taken where the pages are silent:
 natural-log LSE; shard of global token t is (t // I) mod S; with ``causal``
 row r of R sees seq_len - (R - 1 - r) tokens (seq_len counts the R new
@@ -97,16 +105,40 @@ def shard_token_sets(n: int, S: int, I: int) -> list:
     return [t[owner == s] for s in range(S)]
 
 
-def gather_rows(kv_bits: np.ndarray, table_row: np.ndarray, n: int, block_size: int) -> np.ndarray:
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of fp8 E4M3 codes (uint8), the OCP "fn" variant: 1 sign,
+    4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN for
+    S.1111.111; exponent field 0 holds the subnormals m/8 * 2^-6."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def kv_rows_to_f64(rows: np.ndarray, scales=None) -> np.ndarray:
+    """Cache rows [..., 576] in float64: bf16 bit patterns (uint16), or fp8
+    E4M3 codes (uint8) times their per-token scale ``scales`` [...]."""
+    rows = np.asarray(rows)
+    if rows.dtype == np.uint8:
+        return fp8_e4m3_to_f64(rows) * np.asarray(scales, dtype=np.float64)[..., None]
+    return bf16_bits_to_f64(rows)
+
+
+def gather_rows(kv_bits: np.ndarray, table_row: np.ndarray, n: int, block_size: int,
+                kv_scale=None) -> np.ndarray:
     """Logical KV rows 0..n-1 of one request from the paged cache, in float64.
 
     Token t lives in physical block ``table_row[t // block_size]`` at slot
-    ``t % block_size``.
+    ``t % block_size``.  An fp8 cache (uint8 codes) comes with ``kv_scale``
+    [num_blocks, block_size], the per-token factor of its whole row.
     """
     t = np.arange(n, dtype=np.int64)
     phys = np.asarray(table_row, dtype=np.int64)[t // block_size]
     slot = t % block_size
-    return bf16_bits_to_f64(kv_bits[phys, slot, :])
+    return kv_rows_to_f64(kv_bits[phys, slot, :], None if kv_scale is None else kv_scale[phys, slot])
 
 
 def attention_row(q: np.ndarray, K: np.ndarray, scale: float):
@@ -131,11 +163,13 @@ def attention_row(q: np.ndarray, K: np.ndarray, scale: float):
 
 def mla_decode_oracle(q_bits, kv_bits, block_table, seq_lens, num_shards, interleave,
                       scale, causal=True, block_size=None, requests=None, heads=None,
-                      with_shards=True):
+                      with_shards=True, kv_scale=None):
     """Unsplit and per-shard MLA decode attention in float64.
 
     Arguments follow the library's layout: q_bits uint16 [B, R, H, 576] (bf16
-    bits), kv_bits uint16 [num_blocks, block_size, 576], block_table int
+    bits), kv_bits uint16 [num_blocks, block_size, 576] (bf16 bits) or uint8
+    (fp8 E4M3 codes, with ``kv_scale`` float [num_blocks, block_size]: a
+    token's row is its codes' values times its scale), block_table int
     [B, max_blocks], seq_lens int [B].  ``requests`` / ``heads`` restrict the
     evaluation to a subset (the other entries stay NaN).
 
@@ -162,7 +196,7 @@ def mla_decode_oracle(q_bits, kv_bits, block_table, seq_lens, num_shards, interl
     for b in req:
         L = int(seq_lens[b])
         n_max = max(row_length(L, R, r, causal) for r in range(R))
-        K_all = gather_rows(kv_bits, block_table[b], n_max, block_size)
+        K_all = gather_rows(kv_bits, block_table[b], n_max, block_size, kv_scale)
         for r in range(R):
             n = row_length(L, R, r, causal)
             K = K_all[:n]

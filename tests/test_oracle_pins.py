@@ -594,3 +594,92 @@ def test_planted_gather_mistakes_are_caught(monkeypatch, mutation):
             caught = True
             break
     assert caught, mutation
+
+
+# --- fp8 E4M3 KV cache ----------------------------------------------------------
+
+def test_fp8_codes_decode_exactly():
+    """All 256 codes against torch's float8_e4m3fn (a library routine) and
+    the field-by-field decode of the brute-force helper; closed forms."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = mla_oracle.fp8_e4m3_to_f64(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, lib, equal_nan=True)
+    assert np.array_equal(got, np.array([_brute.fp8_to_float(c) for c in codes]), equal_nan=True)
+    closed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+              0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in closed.items():
+        assert got[c] == v, hex(c)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.count_nonzero(np.isnan(got)) == 2
+
+
+FP8_CASES = [
+    # seed, B, R, H, lens, S, I, bs, causal
+    (21, 2, 3, 2, (17, 0), 3, 2, 4, True),
+    (22, 1, 2, 2, (30,), 4, 1, 8, False),
+    (23, 2, 4, 1, (5, 3), 2, 2, 4, True),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES)
+def test_fp8_oracle_matches_brute_force(case):
+    """fp8 rows with per-token scales (some of them far from 1): the oracle
+    against the brute-force attention that decodes each code by its fields."""
+    from workloads import to_fp8
+    seed, B, R, H, lens, S, I, bs, causal = case
+    w = to_fp8(_tiny(seed, B=B, R=R, H=H, lens=lens, S=S, I=I, bs=bs, causal=causal))
+    rng = np.random.default_rng(seed)
+    w.kv_scale = (w.kv_scale * np.exp2(rng.integers(-20, 21, size=w.kv_scale.shape))).astype(np.float32)
+    got = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, S, I, w.scale, causal,
+                                   kv_scale=w.kv_scale)
+    out, lse, lse_sh, out_sh = _brute.brute_decode(
+        w.q_bits.tolist(), w.kv_bits.tolist(), w.block_table.tolist(), w.seq_lens.tolist(),
+        S, I, w.scale, causal, kv_scale=w.kv_scale.tolist())
+    np.testing.assert_allclose(got["out"], np.array(out), rtol=1e-12, atol=1e-12)
+    # scales up to 2^20 make LSEs of order 1e6: compare relatively
+    np.testing.assert_allclose(got["lse_final"], np.array(lse), rtol=1e-13, atol=1e-12)
+    np.testing.assert_allclose(got["lse_shard"], np.array(lse_sh), rtol=1e-13, atol=1e-12)
+    assert np.array_equal(np.isneginf(got["lse_shard"]), np.isneginf(np.array(lse_sh)))
+
+
+def test_fp8_rows_equal_their_dequantised_bf16_values():
+    """A row whose scaled fp8 values are exactly representable in bf16 gives
+    the bf16 oracle's result: scale 2^k times codes with 3 mantissa bits."""
+    from workloads import to_fp8
+    w = _tiny(31, B=1, R=1, H=2, lens=(20,), S=2, I=1, bs=4)
+    f = to_fp8(w)
+    f.kv_scale = np.exp2(np.random.default_rng(3).integers(-4, 5, size=f.kv_scale.shape)).astype(np.float32)
+    vals = mla_oracle.fp8_e4m3_to_f64(f.kv_bits) * f.kv_scale[..., None].astype(np.float64)
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # exact: <= 4 significant bits
+    a = oracle.mla_decode_oracle(f.q_bits, f.kv_bits, f.block_table, f.seq_lens, 2, 1, f.scale, kv_scale=f.kv_scale)
+    b = oracle.mla_decode_oracle(f.q_bits, bits, f.block_table, f.seq_lens, 2, 1, f.scale)
+    for k in ("out", "lse_final", "lse_shard"):
+        assert np.array_equal(np.nan_to_num(a[k], nan=7.0), np.nan_to_num(b[k], nan=7.0)), k
+
+
+def _fp8_scale_on_keys_only(rows, scales=None):
+    rows = np.asarray(rows)
+    if rows.dtype != np.uint8:
+        return _orig_kv_rows(rows)
+    v = mla_oracle.fp8_e4m3_to_f64(rows) * np.asarray(scales, dtype=np.float64)[..., None]
+    v[..., :512] = mla_oracle.fp8_e4m3_to_f64(rows[..., :512])  # V part left unscaled
+    return v
+
+
+_orig_kv_rows = mla_oracle.kv_rows_to_f64
+
+
+def _fp8_as_e5m2(codes):
+    return torch.from_numpy(np.asarray(codes, dtype=np.uint8)).view(torch.float8_e5m2).double().numpy()
+
+
+@pytest.mark.parametrize("mutation", ["scale_keys_only", "e5m2_decode"])
+def test_planted_fp8_mistakes_are_caught(monkeypatch, mutation):
+    if mutation == "scale_keys_only":
+        monkeypatch.setattr(mla_oracle, "kv_rows_to_f64", _fp8_scale_on_keys_only)
+    else:
+        monkeypatch.setattr(mla_oracle, "fp8_e4m3_to_f64", _fp8_as_e5m2)
+    with pytest.raises(AssertionError):
+        for case in FP8_CASES:
+            test_fp8_oracle_matches_brute_force(case)

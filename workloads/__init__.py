@@ -4,6 +4,7 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_rne_bits,
     build,
+    to_fp8,
     tiny,
     batch_decode,
     long_context,

@@ -54,6 +54,11 @@ class Workload:
     scale: float
     causal: bool = True
     unique_kv_tokens: int = 0   # distinct cache rows the requests reference
+    kv_scale: np.ndarray = None  # fp8 caches: float32 [num_blocks, block_size] per-token scales
+
+    @property
+    def kv_format(self):
+        return "fp8" if self.kv_bits.dtype == np.uint8 else "bf16"
 
     @property
     def B(self):
@@ -86,7 +91,7 @@ class Workload:
             "sum_seq_len": int(self.seq_lens.astype(np.int64).sum()),
             "max_seq_len": int(self.seq_lens.max()) if self.B else 0,
             "unique_kv_tokens": int(self.unique_kv_tokens),
-            "causal": bool(self.causal), "softmax_scale": self.scale,
+            "causal": bool(self.causal), "softmax_scale": self.scale, "kv": self.kv_format,
         }
 
 
@@ -160,6 +165,29 @@ def build(name, seq_lens, R, H, num_shards, interleave, *, seed, block_size=64,
                     interleave=interleave, scale=scale, causal=causal,
                     unique_kv_tokens=shared_blocks * block_size + sum(
                         int(L) - shared_blocks * block_size for L in seq_lens if L > 0))
+
+
+def to_fp8(w, name=None):
+    """The same workload with its cache stored as fp8 E4M3 codes plus one
+    float32 scale per token: scale = (largest |value| of the row) / 448, the
+    codes the row divided by it, rounded to nearest even (torch's E4M3 "fn"
+    conversion).  NaN rows (poison) stay NaN."""
+    import torch
+    vals = (w.kv_bits.astype(np.uint32) << 16).view(np.float32)
+    nb, bs, _ = vals.shape
+    codes = np.empty(vals.shape, dtype=np.uint8)
+    scales = np.empty((nb, bs), dtype=np.float32)
+    flat_v, flat_c, flat_s = vals.reshape(-1, ROW), codes.reshape(-1, ROW), scales.reshape(-1)
+    for lo in range(0, flat_v.shape[0], 65536):
+        hi = min(flat_v.shape[0], lo + 65536)
+        v = flat_v[lo:hi]
+        amax = np.max(np.abs(v), axis=1)
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        sc = np.where(np.isnan(amax), np.float32(1.0), sc)
+        x = np.clip(v / sc[:, None], -448.0, 448.0)  # NaN stays NaN
+        flat_c[lo:hi] = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        flat_s[lo:hi] = sc
+    return dataclasses.replace(w, name=name or (w.name + "_fp8"), kv_bits=codes, kv_scale=scales)
 
 
 # ---------------------------------------------------------------------------
