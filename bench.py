@@ -59,6 +59,8 @@ def parse():
                          "HBM-fed step's)")
     ap.add_argument("--no-merge", action="store_true",
                     help="skip the timing of the two-way prefix/suffix merge")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the fp8 KV-cache variant of the workload")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the timing of the chunked-context KV gather")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -237,6 +239,65 @@ def merge_leg(mla, dev, launches):
             "frac": gbps / HBM_PEAK_GBPS}
 
 
+def fp8_leg(mla, dev, launches, min_set_mb):
+    """The same long-context workload with its cache stored as fp8 E4M3 codes
+    plus one float32 scale per token (580 bytes per token instead of 1152):
+    the partial kernel's own duration (HIP events the library records on its
+    stream, cycling cache copies past the Infinity Cache), and the whole step
+    (back-to-back steps between two events)."""
+    import torch
+    import workloads
+    w = workloads.to_fp8(workloads.long_context(1))
+    q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    kv_mb = (w.kv_bits.nbytes + w.kv_scale.nbytes) / 1e6
+    copies = max(1, math.ceil(min_set_mb / kv_mb))
+    kvs = [(torch.from_numpy(w.kv_bits).to(dev), torch.from_numpy(w.kv_scale).to(dev)) for _ in range(copies)]
+    S, I = w.num_shards, w.interleave
+    a = mla.decode_args(q, kvs[0][0], bt, sl, S, I, w.scale, w.causal, kv_scale=kvs[0][1])
+    ws = mla.new_workspace(a, dev)
+    out = torch.empty((w.B, w.R, w.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((S, w.B, w.R, w.H), dtype=torch.float32, device=dev)
+    lf = torch.empty((w.B, w.R, w.H), dtype=torch.float32, device=dev)
+
+    def step(i, events=None):
+        kv, ks = kvs[i % copies]
+        mla.mla_split_decode(q, kv, bt, sl, S, I, w.scale, w.causal, out=out, lse=lse, lse_final=lf,
+                             workspace=ws, events=events, kv_scale=ks)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        step(i, events=e)
+    torch.cuda.synchronize()
+    part = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    comb = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(launches):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / launches
+    tokens = int(w.seq_lens.astype(np.int64).sum())
+    kv_bytes = tokens * (576 + 4)
+    kb = kv_bytes + w.B * w.R * w.H * (ROW_BYTES + 4 * w.num_shards + 1024)
+    gbps = kb / (part / 1e3) / 1e9
+    return {"workload": w.name, "kv_bytes_per_token": 580, "kv_copies_cycled": copies,
+            "partial_kernel_ms": part, "combine_kernel_ms": comb, "ms_per_step": step_ms,
+            "value": tokens / (step_ms / 1e3), "unit": "KV tokens/s",
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "kernel": "mla::partial_kernel<true>",
+                         "bytes_per_launch": kb}}
+
+
 def gather_leg(mla, dev, steps):
     """Time the chunked-context KV gather of the 120k-token run's cached
     context: one step gathers every chunk of the plan (each request's whole
@@ -388,6 +449,8 @@ def main():
     merge = None if args.no_merge else merge_leg(mla, dev, args.event_steps + 2)
     # the chunked-context KV gather (the prefill side of the same shards)
     gather = None if args.no_gather else gather_leg(mla, dev, args.event_steps)
+    # the same decode over an fp8 cache
+    fp8 = None if args.no_fp8 else fp8_leg(mla, dev, args.event_steps, args.min_kv_set_mb)
 
     # K steps in one graph, replayed between synchronisations
     K = args.steps
@@ -451,6 +514,8 @@ def main():
         rec["merge_states"] = merge
     if gather is not None:
         rec["context_gather"] = gather
+    if fp8 is not None:
+        rec["fp8_kv"] = fp8
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

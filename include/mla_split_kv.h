@@ -24,6 +24,13 @@
  * rows that share the request's KV ("perf(mla): fuse K3 DCP verification
  * queries", local-inference-lab/vllm PR 565 page, "Summary").
  *
+ * The cache may be stored as fp8: the PR 565 page's dense-MLA metadata
+ * review-fix commit text runs verification plans on fp8 KV, and the
+ * "FlashMLA sparse: DCP on the fp8_ds_mla mixed-batch path" page names an fp8
+ * cache format, but neither fixes a row layout.  Here an fp8 row is 576 E4M3
+ * codes plus one float32 scale per token (kv_format, kv_scale); the attention
+ * is the same as over the rows' exact values code * scale.
+ *
  * Conventions
  * -----------
  * - LSE is the natural-log log-sum-exp, float32.
@@ -67,6 +74,13 @@ enum {
 
 enum { MLA_HEAD_DIM = 576, MLA_V_DIM = 512 };
 
+/* Storage of the KV cache rows (mla_decode_args.kv_format). */
+enum {
+  MLA_KV_BF16 = 0,     /* 576 bf16 values per token                                     */
+  MLA_KV_FP8_E4M3 = 1  /* 576 fp8 E4M3 codes (OCP "fn" encoding) per token, with one    */
+                       /* float32 scale per token in kv_scale: value = code * scale      */
+};
+
 /* Bits of a decode call's fault word. */
 enum {
   MLA_FAULT_BLOCK_ID = 1, /* a referenced block_table entry outside [0, num_blocks)      */
@@ -94,6 +108,10 @@ typedef struct mla_decode_args {
   int32_t interleave;         /* I >= 1: token t -> shard (t / I) % S                    */
   float softmax_scale;        /* multiplies q.k before the softmax, e.g. 1/sqrt(192)     */
   int32_t causal;             /* nonzero: verification rows see a causal tail            */
+  int32_t kv_format;          /* MLA_KV_BF16 (0, the default) or MLA_KV_FP8_E4M3: then    */
+                              /* kv_cache holds uint8 codes [num_blocks, block_size, 576] */
+  const float* kv_scale;      /* fp8 only: device float32 [num_blocks, block_size], the   */
+                              /* scale of each token's whole row; ignored for bf16        */
 } mla_decode_args;
 
 /* Bytes of device workspace the two decode entry points need for `a`

@@ -37,6 +37,8 @@ class MlaDecodeArgs(ctypes.Structure):
         ("interleave", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
+        ("kv_scale", ctypes.c_void_p),
     ]
 
 
@@ -139,8 +141,15 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal=True):
-    """Validate the decode inputs and build the C argument struct."""
+KV_BF16, KV_FP8_E4M3 = 0, 1
+
+
+def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal=True,
+                kv_scale=None):
+    """Validate the decode inputs and build the C argument struct.
+
+    kv_cache is bf16, or fp8 E4M3 codes (torch.float8_e4m3fn or uint8) with
+    ``kv_scale`` float32 [num_blocks, block_size], one scale per token."""
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
         raise ValueError("q must be [B, R, H, 576]")
     B, R, H, _ = q.shape
@@ -148,7 +157,16 @@ def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, soft
     _need(q, "q", torch.bfloat16, device=dev)
     if kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM:
         raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
-    _need(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    fp8 = kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        _need(kv_cache, "kv_cache", kv_cache.dtype, device=dev)
+        if kv_scale is None:
+            raise ValueError("an fp8 kv_cache needs kv_scale [num_blocks, block_size]")
+        _need(kv_scale, "kv_scale", torch.float32, tuple(kv_cache.shape[:2]), dev)
+    else:
+        _need(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+        if kv_scale is not None:
+            raise ValueError("kv_scale is for fp8 caches only")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks_per_seq]")
     _need(block_table, "block_table", torch.int32, device=dev)
@@ -162,6 +180,8 @@ def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, soft
     a.num_shards, a.interleave = int(num_shards), int(interleave)
     a.softmax_scale = float(softmax_scale)
     a.causal = 1 if causal else 0
+    a.kv_format = KV_FP8_E4M3 if fp8 else KV_BF16
+    a.kv_scale = kv_scale.data_ptr() if fp8 else None
     return a
 
 
@@ -198,15 +218,17 @@ def new_workspace(args: MlaDecodeArgs, device):
 
 def mla_split_decode(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
                      causal=True, out=None, lse=None, lse_final=None, workspace=None,
-                     want_lse_final=True, events=None):
+                     want_lse_final=True, events=None, kv_scale=None):
     """Split-KV decode of every shard plus the LSE combine.
 
     ``events``: optional (begin, mid, end) torch.cuda.Event objects, already
     recorded once, that the library records around its partial and combine
     kernels (calls mla_split_decode_timed).
+    ``kv_scale``: the per-token scales of an fp8 cache.
     Returns (out bf16 [B,R,H,512], lse fp32 [S,B,R,H], lse_final fp32 [B,R,H] or None).
     """
-    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal)
+    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
+                    kv_scale)
     B, R, H, _ = q.shape
     dev = q.device
     if out is None:
@@ -235,12 +257,13 @@ def mla_split_decode(q, kv_cache, block_table, seq_lens, num_shards, interleave,
 
 def mla_shard_decode_partial(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
                              causal=True, shard_begin=0, shard_count=None, out_partial=None, lse=None,
-                             workspace=None):
+                             workspace=None, kv_scale=None):
     """Partial attention of shards [shard_begin, shard_begin + shard_count).
 
     Returns (out_partial fp32 [shard_count,B,R,H,512], lse fp32 [shard_count,B,R,H]).
     """
-    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal)
+    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
+                    kv_scale)
     B, R, H, _ = q.shape
     dev = q.device
     sc = num_shards - shard_begin if shard_count is None else shard_count

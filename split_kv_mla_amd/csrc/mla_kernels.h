@@ -72,9 +72,20 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Item partial rows whose largest |o| is at most this are stored as fp16.
 constexpr float kHalfPartialMax = 2.0f;
 
+// fp8 KV tiles (576 E4M3 codes per token and one float32 scale per token):
+// each wavefront's 8 tokens fill a slice laid out [piece][token] in 16-byte
+// units (piece p of the slice's token tau at 128 p + 16 tau, 36 pieces), then
+// the 8 scales.  The slice stride is 128 modulo the 256-byte bank width, so
+// the K reads (32 tokens, one piece) and the transposing V reads (8 tokens of
+// two slices, 16 bytes each) spread over the banks.
+constexpr int kWave8Bytes = 4736;
+constexpr int kScale8Off = 36 * 128;
+constexpr int kTile8Bytes = 4 * kWave8Bytes;  // 18944
+static_assert(kScale8Off + 32 <= kWave8Bytes && kWave8Bytes % 256 == 128, "fp8 tile layout");
+
 struct DecodeParams {
   const uint16_t* q;         // bf16 [B, R, H, 576]
-  const uint16_t* kv;        // bf16 [num_blocks, block_size, 576]
+  const uint16_t* kv;        // bf16 [num_blocks, block_size, 576], or fp8 E4M3 codes of that shape
   const int32_t* table;      // [B, max_blocks]
   const int32_t* seq_lens;   // [B]
   void* part_o;              // [items_cap, rows_total] slots of 512 fp32 (or 512 fp16 in the first half)
@@ -91,6 +102,10 @@ struct DecodeParams {
   int32_t slots;             // workgroup slots per row group: 8 * floor(32 / row_groups)
   float c_log2;              // softmax_scale * log2(e)
   int32_t causal;
+  // fp8 caches: float32 [num_blocks, block_size], the row scale of each token
+  // (last: the fields above keep the kernel-argument offsets the bf16
+  // kernel's register allocation was tuned with)
+  const float* kv_scale;
 };
 
 // ---------------------------------------------------------------- helpers
@@ -400,6 +415,16 @@ __device__ __forceinline__ void mfma_vgpr_first(f32x16& s, const bf16x8& a, cons
 __device__ __forceinline__ void mfma_vgpr_next(f32x16& s, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b) : "memory");
 }
+// The same products when operand a was just written by a VALU instruction
+// (an fp8 fragment converted to bf16): a matrix product reading a VGPR that
+// a VALU instruction wrote needs 2 wait states, which the compiler inserts
+// for its own products but cannot for an assembly one.
+__device__ __forceinline__ void mfma_vgpr_first_valu(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_vgpr_next_valu(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b) : "memory");
+}
 __device__ __forceinline__ void mfma_vgpr_done(f32x16& s) { asm volatile("s_nop 11" : "+v"(s)); }
 
 // 16 bytes per lane stored with system-scope coherence (sc0 sc1): written
@@ -424,6 +449,29 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// 8 fp8 E4M3 codes -> 8 bf16 values, exactly (every E4M3 value is a bf16
+// value; the conversion's scale is 1).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 r) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ u32x2 lds_read_b64(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Transposing 8-bit read: lanes 2r and 2r+1 of each 16-lane group give the
+// two 8-byte halves of row r (r < 8); lane j of the group receives byte j of
+// rows 0..7.
+__device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Query rows row0 .. row0+31 of request b (one wavefront's rows) copied by
 // LDS-DMA into the ring stage at `dst`, laid out as [64-column group][row]
 // [16-byte piece] with the piece slot XOR-keyed by row % 8: each load covers 8
@@ -445,7 +493,12 @@ __device__ __forceinline__ void copy_q_rows(const DecodeParams& p, int b, int ro
 
 // ------------------------------------------------------------ partial kernel
 
+template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
+  // LDS bytes of one ring stage, and LDS-DMA loads per wavefront per tile
+  constexpr int kStageBytes = kFp8 ? kTile8Bytes : kTileBytes;
+  constexpr int kDma = kFp8 ? 6 : 9;
+  // the ring also stages the query rows (36 KiB per wavefront) and the partial rows
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
   __shared__ int tbl[kTableCache];
   __shared__ int starts[kPlanPairsLds + 1];
@@ -518,13 +571,16 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     const int g = lane >> 5;  // which half of the wavefront
     const int l32 = lane & 31;
     // this wavefront's slice of every ring stage (wave-uniform: a scalar register)
-    const uint32_t wave_lds = lds_ring + (uint32_t)(wave * 9 * 1024);
+    const uint32_t wave_lds = lds_ring + (uint32_t)(wave * (kFp8 ? kWave8Bytes : 9 * 1024));
     const int lane_o = lane;
-    // DMA role: lane loads token tau of each tile, 16-byte pieces (lane_o & 7) ^ swz
-    // of each 128-byte group.  Slot layout of a tile in LDS, in 16-byte units:
-    //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau))
-    const int dma_tau = wave * 8 + (lane_o >> 3);
-    const int dma_swz = ((lane_o & 7) ^ piece_swizzle(dma_tau)) * 16;
+    // DMA role.  bf16: lane loads token tau, 16-byte pieces (lane_o & 7) ^ swz of
+    // each 128-byte group; slot layout of a tile in LDS, in 16-byte units:
+    //   576 * (tau / 8) + 64 * (piece / 8) + 8 * (tau % 8) + ((piece % 8) ^ piece_swizzle(tau)).
+    // fp8: lane loads token tau = 8 wave + lane % 8, pieces lane / 8 + 8 i of
+    // its row (the slice's [piece][token] layout), the rope pieces (lanes
+    // below 32) and the token's scale (lanes below 8).
+    const int dma_tau = kFp8 ? wave * 8 + (lane_o & 7) : wave * 8 + (lane_o >> 3);
+    const int dma_swz = kFp8 ? 16 * (lane_o >> 3) : ((lane_o & 7) ^ piece_swizzle(dma_tau)) * 16;
 
     const int pair = pa.pair;
     const int b = pair / p.shard_count;
@@ -595,10 +651,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     bad = block_any(bad, scratch + 12, wave, lane);
 
 
-    // DMA source of this lane's 16-byte pieces of tile kk: tiles at or past nt
+    // Cache row of this lane's DMA token of tile kk: tiles at or past nt
     // re-read the item's last tile (the prologue's spare stages), and rows past
     // the end re-read the last valid row (masked later).
-    auto tile_src = [&](int kk) -> const char* {
+    auto tile_src = [&](int kk) {
       kk = min(kk, tile1 - 1);
       int j = kk * kTile + dma_tau;
       j = j < n_bs ? j : n_bs - 1;
@@ -607,13 +663,24 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
                                   : global_pos(j, S, I, s);
       const int phys = tbl[(t >> p.bs_log2) - blk_lo];
       const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
-      return reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
+      // fp8: the row index (its codes and its scale are loaded from it); bf16:
+      // this lane's first byte
+      if constexpr (kFp8) return kvrow;
+      else return reinterpret_cast<const char*>(p.kv) + kvrow * (kHeadDim * 2) + dma_swz;
     };
-    // 9 loads per wavefront: its 8 tokens x 1152 bytes of the tile into `stage`.
-    auto issue_src = [&](const char* src, int stage) {
-      const uint32_t dst = wave_lds + (uint32_t)(stage * kTileBytes);
+    // kDma loads per wavefront: its 8 tokens of the tile into `stage`.
+    auto issue_src = [&](auto src_or_row, int stage) {
+      const uint32_t dst = wave_lds + (uint32_t)(stage * kStageBytes);
+      if constexpr (kFp8) {
+        const char* src = reinterpret_cast<const char*>(p.kv) + src_or_row * kHeadDim + dma_swz;
 #pragma unroll
-      for (int i = 0; i < 9; ++i) dma16(src + 128 * i, dst + 1024 * i);
+        for (int i = 0; i < 4; ++i) dma16(src + 128 * i, dst + 1024 * i);
+        if (lane_o < 32) dma16(src + 512, dst + 4096);
+        if (lane_o < 8) dma4(p.kv_scale + src_or_row, dst + kScale8Off);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) dma16(src_or_row + 128 * i, dst + 1024 * i);
+      }
     };
     auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
@@ -665,33 +732,71 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         voff1[e] = 128 * (4 * (lane_r >> 5) + rr) + 16 * (pc ^ f1) + 8 * (cc & 1);
         voff2[e] = 9216 + 128 * (4 * (lane_r >> 5) + rr) + 16 * (pc ^ f2) + 8 * (cc & 1);
       }
-      // K fragment db (A of S^T = K Q^T): token l32, columns 16*db + 8*g .. +7.
+      // fp8 reads: the K fragment is 8 codes of token l32 (piece db, half g);
+      // the V fragment is one transposing read: lane i of 16-lane group
+      // (g, h) addresses token 4g + i/2 (+4 when i/2 >= 4) of the 16-token half,
+      // half i % 2 of piece 2 db + h.
+      const int kbase8 = ((lane_r & 31) >> 3) * kWave8Bytes + 16 * (lane_r & 7) + 8 * (lane_r >> 5);
+      const int r8 = (lane_r & 15) >> 1;
+      const int vtau8 = 4 * (lane_r >> 5) + r8 + (r8 >= 4 ? 4 : 0);
+      const int vbase8 = (vtau8 >> 3) * kWave8Bytes + 16 * (vtau8 & 7) + 8 * (lane_r & 1) + 128 * h16;
+      // K fragment db (A of S^T = K Q^T): token l32, columns 16*db + 8*g .. +7
+      // (raw: fp8 codes until k_val converts them).
       auto k_frag = [&](const char* buf, int db) {
-        return lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+        if constexpr (kFp8) return lds_read_b64(buf + kbase8 + 128 * db);
+        else return lds_read_b128(buf + koff[db & 3] + 1024 * (db >> 2));
+      };
+      auto k_val = [&](const auto& raw) -> bf16x8 {
+        if constexpr (kFp8) return fp8x8_to_bf16(raw);
+        else return raw;
       };
       // V fragment f = 16*kb + db (A of O^T = V^T P^T): columns 32*db + l32 of
       // tokens 16*kb + (8*g .. +7) in the order the P^T fragment uses.
       auto v_frag = [&](const char* buf, int f) {
         const int kb = f >> 4, db = f & 15;
-        const int off = 18432 * kb + 1024 * (db >> 1);
-        const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
-        const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (kFp8) {
+          return lds_read_tr8(buf + vbase8 + 2 * kWave8Bytes * kb + 256 * db);
+        } else {
+          const int off = 18432 * kb + 1024 * (db >> 1);
+          const bf16x4 lo = lds_read_tr(buf + voff1[db & 1] + off);
+          const bf16x4 hi = lds_read_tr(buf + voff2[db & 1] + off);
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      using KRaw = decltype(k_frag(ring, 0));
+      using VRaw = decltype(v_frag(ring, 0));
+      // fp8: the scales of the lane's 16 score tokens 8*(i/4) + 4*g + i%4 of
+      // the tile in `buf` (a token's score and its V weight carry its scale)
+      auto tile_scales = [&](const char* buf) {
+        f32x16 ks{};
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(buf + q4 * kWave8Bytes + kScale8Off + 16 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ks[4 * q4 + e] = v[e];
+          }
+        }
+        return ks;
       };
 
       // tiles kept in flight ahead of the tile being consumed
       constexpr int kAheadTiles = kMaxOnly ? kStages - 1 : kLead;
       if (!prologue_issued)
         for (int k = 0; k < kAheadTiles; ++k) issue_tile(tile0 + k, k);
-      const char* next_src = tile_src(tile0 + kAheadTiles);
+      auto next_src = tile_src(tile0 + kAheadTiles);
       float m_walk = -INFINITY;
 
       // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4)):
       // masks the tokens at or past the row's end and returns the softmax
       // reference, or (kMaxOnly) folds the row maximum into m_walk.
       // Branch-free, so that it schedules among the matrix products.
-      auto prep = [&](f32x16& sc, int kt) -> float {
+      auto prep = [&](f32x16& sc, int kt, const f32x16& ks) -> float {
         const int jt = (tile0 + kt) * kTile + 4 * g;
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[i] *= ks[i];
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = (jt + 8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : sc[i];
         float mx = sc[0];
@@ -712,11 +817,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // P_lo, both bf16: a single bf16 P would cost up to 2^-8 of relative
       // weight per token, too much for rows of a few tokens or with outlier
       // values; the pair leaves a residual of at most 2^-16 p.
-      auto make_p = [&](PFrag& pf, const f32x16& sc, float msafe, int kb) {
+      // fp8: the V weight of a token is its softmax numerator times its scale.
+      auto make_p = [&](PFrag& pf, const f32x16& sc, float msafe, int kb, const f32x16& ks) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
+          float x = __builtin_amdgcn_exp2f(fmaf(sc[8 * kb + j], c, -msafe));
           l_run += x;
+          if constexpr (kFp8) x *= ks[8 * kb + j];
           const __bf16 hi = (__bf16)x;
           pf.hi[kb][j] = hi;
           pf.lo[kb][j] = (__bf16)(x - (float)hi);
@@ -728,22 +835,37 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         // memory clobber keeps the reads where they are written)
         constexpr int kAhead = 6;
         f32x16 sc;
-        bf16x8 kf[36];
+        KRaw kf[36];
 #pragma unroll
         for (int db = 0; db < kAhead; ++db) kf[db] = k_frag(buf, db);
+        bf16x8 kc;
+        if constexpr (kFp8) kc = k_val(kf[0]);
 #pragma unroll
         for (int db = 0; db < 36; ++db) {
-          if (db == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
-          else mfma_vgpr_next(sc, kf[db], qf[db]);
+          if constexpr (kFp8) {
+            const bf16x8 kn = db + 1 < 36 ? k_val(kf[db + 1]) : kc;  // converted a product ahead
+            if (db == 0) mfma_vgpr_first_valu(sc, kc, qf[0]);
+            else mfma_vgpr_next_valu(sc, kc, qf[db]);
+            kc = kn;
+          } else {
+            if (db == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
+            else mfma_vgpr_next(sc, kf[db], qf[db]);
+          }
           if (db + kAhead < 36) kf[db + kAhead] = k_frag(buf, db + kAhead);
         }
         mfma_vgpr_done(sc);
         return sc;
       };
-      // PV product i of a tile (64 per tile): fragment i/2, P_hi for even i, P_lo for odd.
-      auto pv_mfma = [&](const bf16x8* vf, const PFrag& pf, int i) {
+      // PV product i of a tile (64 per tile): fragment i/2 (vcur: converted at
+      // the even product), P_hi for even i, P_lo for odd.
+      auto pv_mfma = [&](const VRaw* vf, bf16x8& vcur, const PFrag& pf, int i) {
         const int f = i >> 1, kb = f >> 4, db = f & 15;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);
+        if constexpr (kFp8) {
+          if (!(i & 1)) vcur = k_val(vf[f]);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);
+        } else {
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);
+        }
       };
 
       if constexpr (kMaxOnly) {
@@ -752,16 +874,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           // younger loads in flight are min(2, nt-1-k), or the spare re-reads
           // when the item has fewer than kStages-1 tiles
           const int younger = nt >= kStages - 1 ? min(nt - 1 - k, kStages - 2) : kStages - 2 - k;
-          if (younger >= 2) wait_vmcnt<18>();
-          else if (younger == 1) wait_vmcnt<9>();
+          if (younger >= 2) wait_vmcnt<2 * kDma>();
+          else if (younger == 1) wait_vmcnt<kDma>();
           else wait_vmcnt<0>();
           // every wavefront is past tile k-1: its stage takes tile k+3 (this
           // slow-path walk keeps kStages - 1 tiles in flight)
           lds_barrier();
           if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
           next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
-          f32x16 sc = qk_alone(ring + (k % kStages) * kTileBytes);
-          prep(sc, k);
+          const char* buf = ring + (k % kStages) * kStageBytes;
+          f32x16 sc = qk_alone(buf);
+          prep(sc, k, tile_scales(buf));
         }
         m_ref = m_walk;
       } else {
@@ -770,15 +893,16 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         // accumulator, and tile k+1's P under the last of those products, so
         // the matrix pipe does not wait for the softmax.
         static_assert(kLead == 2 || kLead == 3, "DMA waits below");
-        if constexpr (kLead == 3) wait_vmcnt<18>();  // tile 0 (tiles 1 and 2 in flight)
-        else wait_vmcnt<9>();                        // tile 0 (tile 1 in flight)
+        if constexpr (kLead == 3) wait_vmcnt<2 * kDma>();  // tile 0 (tiles 1 and 2 in flight)
+        else wait_vmcnt<kDma>();                        // tile 0 (tile 1 in flight)
         lds_barrier();
         PFrag pf;
         {
           f32x16 sc = qk_alone(ring);
-          const float msafe = prep(sc, 0);
-          make_p(pf, sc, msafe, 0);
-          make_p(pf, sc, msafe, 1);
+          const f32x16 ks = tile_scales(ring);
+          const float msafe = prep(sc, 0, ks);
+          make_p(pf, sc, msafe, 0, ks);
+          make_p(pf, sc, msafe, 1, ks);
         }
         for (int k = 0; k < nt; ++k) {
           const bool more = k + 1 < nt;
@@ -786,7 +910,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
             // tile k+1 resident: the loads issued so far are the prologue's
             // kLead plus one per earlier iteration that still had a tile to load
             const int younger = kLead + max(0, min(k, nt - kLead)) - (k + 2);
-            if (younger >= 1) wait_vmcnt<9>();
+            if (younger >= 1) wait_vmcnt<kDma>();
             else wait_vmcnt<0>();
           }
           // every wavefront is past iteration k-1 (tile k-1's products): the
@@ -794,16 +918,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           lds_barrier();
           if (k + kLead < nt) issue_src(next_src, (k + kLead) % kStages);
           next_src = tile_src(tile0 + k + kLead + 1);  // clamped past the end: harmless
-          const char* buf = ring + (k % kStages) * kTileBytes;
-          const char* nbuf = ring + ((k + 1) % kStages) * kTileBytes;
+          const char* buf = ring + (k % kStages) * kStageBytes;
+          const char* nbuf = ring + ((k + 1) % kStages) * kStageBytes;
           // O^T[dim][row] += V^T[dim][token] P^T[token][row]: product i uses
           // fragment i/2 (read kVAhead fragments ahead), P_hi for even i, P_lo for odd
           constexpr int kVAhead = 6;
-          bf16x8 vf[32];
+          VRaw vf[32];
+          bf16x8 vcur;
 #pragma unroll
           for (int f = 0; f < kVAhead; ++f) vf[f] = v_frag(buf, f);
           auto pv_step = [&](int i) {
-            pv_mfma(vf, pf, i);
+            pv_mfma(vf, vcur, pf, i);
             if ((i & 1) && (i >> 1) + kVAhead < 32) vf[(i >> 1) + kVAhead] = v_frag(buf, (i >> 1) + kVAhead);
           };
           {
@@ -813,21 +938,31 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
             // score there is masked, so its P is zero and adds nothing.
             constexpr int kAhead = 4;
             f32x16 sc;
-            bf16x8 kf[36];
+            KRaw kf[36];
 #pragma unroll
             for (int db = 0; db < kAhead; ++db) kf[db] = k_frag(nbuf, db);
+            bf16x8 kc;
+            if constexpr (kFp8) kc = k_val(kf[0]);
 #pragma unroll
             for (int i = 0; i < 36; ++i) {
-              if (i == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
-              else mfma_vgpr_next(sc, kf[i], qf[i]);
+              if constexpr (kFp8) {
+                const bf16x8 kn = i + 1 < 36 ? k_val(kf[i + 1]) : kc;  // converted a product ahead
+                if (i == 0) mfma_vgpr_first_valu(sc, kc, qf[0]);
+                else mfma_vgpr_next_valu(sc, kc, qf[i]);
+                kc = kn;
+              } else {
+                if (i == 0) mfma_vgpr_first(sc, kf[0], qf[0]);
+                else mfma_vgpr_next(sc, kf[i], qf[i]);
+              }
               if (i + kAhead < 36) kf[i + kAhead] = k_frag(nbuf, i + kAhead);
               pv_step(i);
             }
             mfma_vgpr_done(sc);
-            const float msafe = prep(sc, k + 1);
+            const f32x16 ks = tile_scales(nbuf);
+            const float msafe = prep(sc, k + 1, ks);
             PFrag pn;
-            make_p(pn, sc, msafe, 0);
-            make_p(pn, sc, msafe, 1);
+            make_p(pn, sc, msafe, 0, ks);
+            make_p(pn, sc, msafe, 1, ks);
 #pragma unroll
             for (int i = 36; i < 64; ++i) pv_step(i);
             pf = pn;

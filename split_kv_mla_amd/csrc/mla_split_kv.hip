@@ -35,6 +35,8 @@ int check_args(const mla_decode_args* a) {
     return MLA_ERR_INVALID_ARG;
   if (!(a->softmax_scale > 0.f) || !std::isfinite(a->softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (a->batch > 0 && (!a->q || !a->kv_cache || !a->block_table || !a->seq_lens)) return MLA_ERR_INVALID_ARG;
+  if (a->kv_format != MLA_KV_BF16 && a->kv_format != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  if (a->kv_format == MLA_KV_FP8_E4M3 && a->batch > 0 && !a->kv_scale) return MLA_ERR_INVALID_ARG;
   if (a->rows > 8 || (int64_t)a->rows * a->heads > 1024) return MLA_ERR_UNSUPPORTED;
   const int lg = ilog2_exact(a->block_size);
   if (lg < 0 || a->block_size > 1024) return MLA_ERR_UNSUPPORTED;
@@ -96,6 +98,7 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   mla::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(a->q);
   p.kv = static_cast<const uint16_t*>(a->kv_cache);
+  p.kv_scale = a->kv_format == MLA_KV_FP8_E4M3 ? a->kv_scale : nullptr;
   p.table = a->block_table;
   p.seq_lens = a->seq_lens;
   p.faults = static_cast<int32_t*>(ws);
@@ -129,7 +132,10 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
 
 int launch_partial(const mla::DecodeParams& p, hipStream_t stream) {
   // persistent: one workgroup per compute unit walks all (item, row group) units
-  hipLaunchKernelGGL(mla::partial_kernel, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
+  if (p.kv_scale)
+    hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(mla::partial_kernel<false>, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -354,3 +354,18 @@ def test_gather_rejects_bad_arguments_without_launching():
     a = _gather_args()
     a.cu_rows = 0
     assert lib.mla_gather_context_chunk(ctypes.byref(a), good, 64, None, vp(0)) == -1
+
+
+def test_fp8_cache_needs_its_scales():
+    lib = m.load_library()
+    null = ctypes.c_void_p(0)
+    a = _args()
+    a.kv_format = 1  # fp8 E4M3 without kv_scale
+    assert lib.mla_workspace_bytes(ctypes.byref(a)) == 0
+    assert lib.mla_split_decode(ctypes.byref(a), ctypes.c_void_p(8), ctypes.c_void_p(8), null,
+                                ctypes.c_void_p(8), 1 << 40, null) == -1
+    a.kv_format = 2  # no such format
+    a.kv_scale = 0x1000
+    assert lib.mla_workspace_bytes(ctypes.byref(a)) == 0
+    a.kv_format = 1
+    assert lib.mla_workspace_bytes(ctypes.byref(a)) > 0
