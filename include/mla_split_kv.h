@@ -81,6 +81,9 @@ enum {
                        /* float32 scale per token in kv_scale: value = code * scale      */
 };
 
+/* Device scratch bytes behind mla_split_decode_static (96 MiB per GPU). */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+
 /* Bits of a decode call's fault word. */
 enum {
   MLA_FAULT_BLOCK_ID = 1, /* a referenced block_table entry outside [0, num_blocks)      */
@@ -203,6 +206,20 @@ int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse
 int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, float* lse_final,
                            void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
                            void* ev_mid, void* ev_end);
+
+/* mla_split_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the partials go to the library's own
+ * static device scratch of MLA_STATIC_SCRATCH_BYTES on the current device,
+ * and the call allocates nothing.  Same arguments (minus the workspace),
+ * results and errors as mla_split_decode, plus MLA_ERR_WORKSPACE_TOO_SMALL
+ * when mla_workspace_bytes(a) exceeds MLA_STATIC_SCRATCH_BYTES (e.g. 16
+ * requests x 4 rows x 128 heads of up to 131072 tokens need 321 MiB).  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race and must
+ * not be issued.  The fault word of such a call is not readable
+ * (device-detected faults still NaN-fill the affected requests' outputs). */
+int mla_split_decode_static(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* stream);
 
 /* The fault word (MLA_FAULT_* bits) of the last decode call enqueued on
  * `stream` with `workspace` (or, given a gather's `faults` pointer, that

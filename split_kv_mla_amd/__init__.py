@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     mla_plan_capacity,
     mla_shard_decode_partial,
     mla_split_decode,
+    mla_split_decode_static,
     mla_workspace_bytes,
     new_workspace,
 )

@@ -94,6 +94,9 @@ def load_library(path: str = LIB_PATH):
     lib.mla_merge_states.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
     lib.mla_merge_states.restype = ctypes.c_int
+    lib.mla_split_decode_static.argtypes = [P(MlaDecodeArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    lib.mla_split_decode_static.restype = ctypes.c_int
     lib.mla_device_faults.argtypes = [ctypes.c_void_p, ctypes.c_void_p, P(ctypes.c_int32)]
     lib.mla_device_faults.restype = ctypes.c_int
     i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -252,6 +255,27 @@ def mla_split_decode(q, kv_cache, block_table, seq_lens, num_shards, interleave,
         handles = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
         _check(lib.mla_split_decode_timed(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(lse_final),
                                           _ptr(workspace), workspace.numel(), _stream(dev), *handles))
+    return out, lse, lse_final
+
+
+STATIC_SCRATCH_BYTES = 96 << 20
+
+
+def mla_split_decode_static(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
+                            out, lse, lse_final=None, causal=True, kv_scale=None):
+    """mla_split_decode into caller-given outputs, with the library's static
+    device scratch as workspace: neither the library nor this binding
+    allocates device memory.  Calls that overlap on one GPU race."""
+    a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
+                    kv_scale)
+    B, R, H, _ = q.shape
+    dev = q.device
+    _need(out, "out", torch.bfloat16, (B, R, H, V_DIM), dev)
+    _need(lse, "lse", torch.float32, (num_shards, B, R, H), dev)
+    if lse_final is not None:
+        _need(lse_final, "lse_final", torch.float32, (B, R, H), dev)
+    _check(load_library().mla_split_decode_static(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(lse_final),
+                                                  _stream(dev)))
     return out, lse, lse_final
 
 

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <algorithm>
+#include <mutex>
 
 #include "mla_kernels.h"
 #include "mla_split_kv.h"
@@ -157,6 +158,31 @@ int launch_combine(const mla::CombineParams& c, int64_t units, int64_t sources, 
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// Scratch of the allocation-free entry point: device memory of the library
+// itself (one copy on every GPU the library runs on, held until the process
+// ends).  In host code `scratch` names a host-side stand-in; its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = MLA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on its first use).
+int static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +295,16 @@ int mla_split_decode(const mla_decode_args* a, void* out, float* lse, float* lse
                      size_t workspace_bytes, void* stream) {
   return mla_split_decode_timed(a, out, lse, lse_final, workspace, workspace_bytes, stream, nullptr, nullptr,
                                 nullptr);
+}
+
+int mla_split_decode_static(const mla_decode_args* a, void* out, float* lse, float* lse_final, void* stream) {
+  int st = check_args(a);
+  if (st != MLA_OK) return st;
+  if (make_plan(a, 0, a->num_shards).total() > kStaticScratchBytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (a->batch == 0) return MLA_OK;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MLA_OK) return st;
+  return mla_split_decode(a, out, lse, lse_final, ws, kStaticScratchBytes, stream);
 }
 
 int mla_device_faults(const void* workspace, void* stream, int32_t* faults) {

@@ -369,3 +369,15 @@ def test_fp8_cache_needs_its_scales():
     assert lib.mla_workspace_bytes(ctypes.byref(a)) == 0
     a.kv_format = 1
     assert lib.mla_workspace_bytes(ctypes.byref(a)) > 0
+
+
+def test_static_entry_rejects_calls_beyond_its_scratch_without_launching():
+    lib = m.load_library()
+    vp = ctypes.c_void_p
+    big = _args(B=16, R=4, H=128, S=8, I=16, max_blocks=2048, num_blocks=30000)  # needs ~321 MiB
+    assert m.mla_workspace_bytes(big) > _binding.STATIC_SCRATCH_BYTES
+    assert lib.mla_split_decode_static(ctypes.byref(big), vp(8), vp(8), None, None) == -3
+    bad = _args(S=0)
+    assert lib.mla_split_decode_static(ctypes.byref(bad), vp(8), vp(8), None, None) == -1
+    empty = _args(B=0)
+    assert lib.mla_split_decode_static(ctypes.byref(empty), None, None, None, None) == 0
