@@ -527,12 +527,23 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   // wavefronts 1-3 copy its rows (a third each) besides their own, so that
   // it does not wait behind the copy's loads to issue them.
   bool q_in_ring = false;
+  // One request whose block-table row fits the LDS table: the whole row is
+  // loaded with the query rows, so no item waits for its table window after
+  // the plan (entries are range-checked where they are used).
+  const bool tbl_whole = p.B == 1 && p.max_blocks <= kTableCache;
   if (p.B == 1 && (int)(blockIdx.x >> 3) < G * (32 / G)) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rg0 = ((int)(blockIdx.x >> 3) % G) * kRowsPerGroup;
     if (wave != 0) {
       copy_q_rows(p, 0, rg0 + wave * kRowsPerWave, threadIdx.x & 63, lds_ring + (uint32_t)(wave * kTileBytes));
       copy_q_rows(p, 0, rg0, threadIdx.x & 63, lds_ring, 12 * (wave - 1), 12 * wave);
+      if (tbl_whole) {
+        const uint32_t tbl_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)tbl;
+        for (int i0 = 64 * (wave - 1); i0 < p.max_blocks; i0 += 192) {
+          const int i = i0 + (int)(threadIdx.x & 63);
+          if (i < p.max_blocks) dma4(p.table + i, __builtin_amdgcn_readfirstlane(tbl_lds + 4u * (uint32_t)i0));
+        }
+      }
     }
     q_in_ring = true;
   }
@@ -600,14 +611,16 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     // The previous unit is done with the ring and the table window.
     __syncthreads();
 
-    // Block-table window of this item (fits kTableCache: U <= tpi_max).
+    // Block-table window of this item (fits kTableCache: U <= tpi_max);
+    // tbl[i] holds entry tbl_base + i of the request's row.
     const int blk_lo = global_pos(tile0 * kTile, S, I, s) >> p.bs_log2;
     const int blk_hi = global_pos(min(tile1 * kTile, n_bs) - 1, S, I, s) >> p.bs_log2;
     const int span = blk_hi - blk_lo + 1;
+    const int tbl_base = tbl_whole ? 0 : blk_lo;
     // The window goes straight to LDS; Q (lane holds row l32, columns
     // 16*db + 8*g .. +7; rows past rows_total load row 0 and never write) is
     // loaded behind it, so the wait for the window leaves Q in flight.
-    {
+    if (!tbl_whole) {
       const int32_t* trow = p.table + (size_t)b * p.max_blocks + blk_lo;
       const uint32_t tbl_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)tbl;
       for (int i0 = 0; i0 < span; i0 += kThreads) {
@@ -640,14 +653,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int db = 0; db < 36; ++db) asm volatile("" : "+v"(qf[db]));
     }
-    bool bad = false;
-    for (int i = tid; i < span; i += kThreads) {
-      const int v = tbl[i];
-      if ((unsigned)v >= (unsigned)p.num_blocks) {  // never address outside the cache
-        tbl[i] = 0;
-        bad = true;
-      }
-    }
+    bool bad = false;  // an entry of the item's window outside the cache (the tile loads clamp it)
+    for (int i = tid; i < span; i += kThreads)
+      if ((unsigned)tbl[blk_lo - tbl_base + i] >= (unsigned)p.num_blocks) bad = true;
     bad = block_any(bad, scratch + 12, wave, lane);
 
 
@@ -661,7 +669,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // global position of local token j (shifts when I is a power of two)
       const int t = p.i_log2 >= 0 ? (((j >> p.i_log2) * S + s) << p.i_log2) | (j & (I - 1))
                                   : global_pos(j, S, I, s);
-      const int phys = tbl[(t >> p.bs_log2) - blk_lo];
+      int phys = tbl[(t >> p.bs_log2) - tbl_base];
+      phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;  // never address outside the cache
       const int64_t kvrow = ((int64_t)phys << p.bs_log2) | (t & bs_mask);
       // fp8: the row index (its codes and its scale are loaded from it); bf16:
       // this lane's first byte
@@ -684,10 +693,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     };
     auto issue_tile = [&](int kk, int stage) { issue_src(tile_src(kk), stage); };
 
-    // Prologue: the walk's first kLead tiles back to back (Q is already in
-    // registers).
-#pragma unroll
-    for (int k = 0; k < kLead; ++k) issue_tile(tile0 + k, k);
+    // Prologue: the walk's first tile (Q is already in registers).  Its
+    // second follows once the first has landed: every workgroup starts at
+    // once, and a burst of two tiles from each would make the first wait for
+    // the second's bytes too.
+    issue_tile(tile0, 0);
 
     f32x16 acc[16];
     float m_ref = -INFINITY;  // fixed softmax reference (base-2 units) of this lane's row
@@ -782,8 +792,14 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
 
       // tiles kept in flight ahead of the tile being consumed
       constexpr int kAheadTiles = kMaxOnly ? kStages - 1 : kLead;
-      if (!prologue_issued)
+      if (!prologue_issued) {
         for (int k = 0; k < kAheadTiles; ++k) issue_tile(tile0 + k, k);
+      } else {
+        // the prologue issued tile 0 alone: the rest of the lead follows it
+        static_assert(kLead == 2, "the prologue's first tile plus one");
+        wait_vmcnt<0>();
+        issue_tile(tile0 + 1, 1);
+      }
       auto next_src = tile_src(tile0 + kAheadTiles);
       float m_walk = -INFINITY;
 
