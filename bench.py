@@ -77,7 +77,8 @@ def parse():
 
 KERNEL_SOURCES = ("split_kv_mla_amd/csrc/mla_kernels.h", "split_kv_mla_amd/csrc/mla_plan.h",
                   "split_kv_mla_amd/csrc/mla_split_kv.hip")
-PARTIAL_KERNEL = "mla::partial_kernel"
+PARTIAL_KERNEL = "mla::partial_kernel<false>"      # the bf16 cache's instantiation
+PARTIAL_KERNEL_FP8 = "mla::partial_kernel<true>"   # the fp8 cache's
 
 
 def kernel_source_sha():
@@ -140,7 +141,7 @@ def summarize_counters(fetch_dir, write_dir, workload_name, calib_mib):
     return rec
 
 
-def load_traffic(workload_name):
+def load_traffic(workload_name, kernel=PARTIAL_KERNEL):
     """HBM bytes per launch of the partial kernel from the committed counter
     summary, or None when there is none or the kernel changed since."""
     path = counters_path(workload_name)
@@ -149,7 +150,7 @@ def load_traffic(workload_name):
     rec = json.load(open(path))
     if rec.get("source_sha") != kernel_source_sha():
         return None
-    k = rec.get("kernels", {}).get(PARTIAL_KERNEL)
+    k = rec.get("kernels", {}).get(kernel)
     if not k or k.get("read_bytes") is None or k.get("write_bytes") is None:
         return None
     return k["read_bytes"] + k["write_bytes"]
@@ -239,7 +240,7 @@ def merge_leg(mla, dev, launches):
             "frac": gbps / HBM_PEAK_GBPS}
 
 
-def fp8_leg(mla, dev, launches, min_set_mb):
+def fp8_leg(mla, dev, launches, min_set_mb, counters_workload):
     """The same long-context workload with its cache stored as fp8 E4M3 codes
     plus one float32 scale per token (580 bytes per token instead of 1152):
     the partial kernel's own duration (HIP events the library records on its
@@ -287,15 +288,15 @@ def fp8_leg(mla, dev, launches, min_set_mb):
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / launches
     tokens = int(w.seq_lens.astype(np.int64).sum())
-    kv_bytes = tokens * (576 + 4)
-    kb = kv_bytes + w.B * w.R * w.H * (ROW_BYTES + 4 * w.num_shards + 1024)
+    kb = tokens * (576 + 4) + w.B * w.R * w.H * ROW_BYTES  # what the partial kernel must read: codes, scales, q
     gbps = kb / (part / 1e3) / 1e9
     return {"workload": w.name, "kv_bytes_per_token": 580, "kv_copies_cycled": copies,
             "partial_kernel_ms": part, "combine_kernel_ms": comb, "ms_per_step": step_ms,
             "value": tokens / (step_ms / 1e3), "unit": "KV tokens/s",
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "kernel": "mla::partial_kernel<true>",
-                         "bytes_per_launch": kb}}
+                         "frac": gbps / HBM_PEAK_GBPS, "kernel": PARTIAL_KERNEL_FP8,
+                         "bytes_per_launch": kb,
+                         "traffic": load_traffic(counters_workload, PARTIAL_KERNEL_FP8)}}
 
 
 def gather_leg(mla, dev, steps):
@@ -458,7 +459,7 @@ def main():
     # the chunked-context KV gather (the prefill side of the same shards)
     gather = None if args.no_gather else gather_leg(mla, dev, args.event_steps)
     # the same decode over an fp8 cache
-    fp8 = None if args.no_fp8 else fp8_leg(mla, dev, args.event_steps, args.min_kv_set_mb)
+    fp8 = None if args.no_fp8 else fp8_leg(mla, dev, args.event_steps, args.min_kv_set_mb, w.name)
 
     # K steps in one graph, replayed between synchronisations
     K = args.steps
