@@ -6,7 +6,9 @@ it, because they involve inline assembly:
 * the score products written as assembly accumulate in VGPRs, and nothing
   reads their result before 12 wait states have passed (the spacing the
   compiler itself uses after a VGPR-form 32x32x16 product);
-* no packed fp32 arithmetic appears in the generated code.
+* no packed fp32 arithmetic appears in the generated code;
+* a 16-byte assembly store's data registers are not overwritten at once, and
+  an assembly product reading a VALU-converted operand waits 2 states.
 """
 
 import os
@@ -111,5 +113,38 @@ def test_wide_store_data_is_not_overwritten_at_once(asm):
                     assert seen >= 2, f"line {i + 1} -> {j + 1}: {x}"
                 seen += 1
             if seen >= 2:
+                break
+    assert checked > 0
+
+
+def test_converted_operands_wait_before_assembly_products(asm):
+    """In the fp8 kernel the score products' K operand is converted from fp8 by
+    VALU instructions; a matrix product that reads a VGPR written by a VALU
+    instruction needs 2 wait states, which the compiler cannot insert before
+    an assembly product.  Every VGPR-form product whose A operand a
+    `v_cvt_scalef32_pk_bf16_fp8` wrote within the previous two instructions
+    must have an `s_nop` of at least 1 in between."""
+    code = [_code(x) for x in asm]
+    checked = 0
+    for i, x in enumerate(code):
+        m = re.match(r"v_mfma_f32_32x32x16_bf16 v\[\d+:\d+\], (v\[\d+:\d+\]), v\[\d+:\d+\], (0|v\[\d+:\d+\])$", x)
+        if not m:
+            continue
+        a = _regs(m.group(1))
+        prev = [y for y in code[max(0, i - 6):i] if y and not y.startswith((";", "."))]
+        waits = 0
+        for y in reversed(prev):
+            n = re.fullmatch(r"s_nop (\d+)", y)
+            if n:
+                waits += int(n.group(1)) + 1
+                continue
+            if y.startswith("v_cvt_scalef32_pk_bf16_fp8"):
+                dst = _regs(y.split(",")[0])
+                if dst & a:
+                    assert waits >= 2, f"line {i + 1}: {x} reads {sorted(dst & a)} right after {y}"
+                    checked += 1
+                break
+            waits += 1
+            if waits >= 2:
                 break
     assert checked > 0
