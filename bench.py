@@ -5,8 +5,9 @@ kernel) over one batch of synthetic inputs resident in HBM.  Default workload:
 the 120k-token long-context request (B=1, R=1, H=128, S=8 virtual shards,
 interleave 1, bf16 N(0,1), 64-token blocks).
 
-Timing: W warm-up steps, then exactly K steps captured in one HIP graph and
-replayed between two device synchronisations; ms_per_step is that wall time
+Timing: W warm-up steps, then exactly K steps captured in one HIP graph; the
+graph is replayed three times untimed (its first replays run slower) and then
+once between two device synchronisations; ms_per_step is that wall time
 divided by K.  The K steps cycle through several copies of the KV cache whose
 total exceeds the 256 MB Infinity Cache, so KV bytes come from HBM.  The
 partial kernel's own duration is measured live with HIP events recorded by the
@@ -43,6 +44,7 @@ METRIC = "KV tokens/s + HBM GB/s (% of peak) for split-KV MLA decode + LSE combi
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 576 * 2
+GRAPH_WARM_REPLAYS = 3  # untimed replays of the captured K-step graph before the timed one
 
 
 def parse():
@@ -473,7 +475,11 @@ def main():
     with torch.cuda.graph(g):
         for i in range(K):
             step(i)
-    g.replay()  # first replay uploads the graph
+    # Untimed replays first: the first replays of a freshly captured graph run
+    # slower (measured: 82-85 µs per step against 74-75 once settled, for both
+    # graph and eager launches), so the timed replay is the fourth.
+    for _ in range(GRAPH_WARM_REPLAYS):
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g.replay()
@@ -496,6 +502,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "graph_warm_replays": GRAPH_WARM_REPLAYS,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
