@@ -402,3 +402,42 @@ def test_fault_word_reports_each_device_fault():
     w.block_table[1, 2] = 2
     _say("[faults] clean again")
     assert _faults_of(w)[:2] == (0, 0)
+
+
+# ------------------------------------------------------------ full block tables
+
+def _sampled_parity(w, heads, tag):
+    """Every request and row, the given heads: out, per-shard LSE, merged LSE."""
+    _say(f"[parity] {tag}: B={w.B} R={w.R} H={w.H} S={w.num_shards} I={w.interleave} "
+         f"every length = {int(w.seq_lens[0])} (full tables of {w.max_blocks} blocks)")
+    out, lse, lf = _run_split(w)
+    ref = oracle.mla_decode_oracle(w.q_bits, w.kv_bits, w.block_table, w.seq_lens, w.num_shards,
+                                   w.interleave, w.scale, w.causal, heads=heads, with_shards=False)
+    hs = list(heads)
+    e1 = assert_out_close(out[:, :, hs], ref["out"][:, :, hs], what=f"{tag} out")
+    e2 = assert_lse_close(lse[:, :, :, hs], ref["lse_shard"][:, :, :, hs], what=f"{tag} lse_shard")
+    e3 = assert_lse_close(lf[:, :, hs], ref["lse_final"][:, :, hs], what=f"{tag} lse_final")
+    assert np.isfinite(out).all() and not np.isnan(lf).any(), f"{tag}: NaN where every input is valid"
+    _say(f"[parity] {tag}: max err out {e1:.2e} lse {e2:.2e} lse_final {e3:.2e}")
+
+
+def test_full_tables_b16_r4_interleave16():
+    """16 requests x 4 rows x 128 heads whose lengths fill 981-block tables:
+    the shape where a plan sized for one piece charge per request (instead of
+    one per request and shard) ran out of item slots."""
+    m = _lib()
+    L = 981 * 64
+    w = build("full_b16_r4", [L] * 16, R=4, H=128, num_shards=8, interleave=16, seed=95,
+              shared_prefix_tokens=L)
+    a = m.decode_args(*to_device(w), w.num_shards, w.interleave, w.scale, w.causal)
+    items, groups = m.mla_plan_capacity(a)
+    _say(f"[parity] full_b16_r4: plan capacity {items} items per row group, {groups} row groups")
+    _sampled_parity(w, [0, 37, 64, 101, 127], "full_b16_r4")
+
+
+def test_full_tables_b64():
+    """64 requests filling 2001-block tables (one shared copy of the blocks)."""
+    L = 2001 * 64
+    w = build("full_b64", [L] * 64, R=1, H=128, num_shards=8, interleave=1, seed=96,
+              shared_prefix_tokens=L)
+    _sampled_parity(w, [5, 90], "full_b64")
