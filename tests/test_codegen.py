@@ -148,3 +148,30 @@ def test_converted_operands_wait_before_assembly_products(asm):
             if waits >= 2:
                 break
     assert checked > 0
+
+
+def test_tile_loops_touch_no_scratch(asm):
+    """The partial kernel keeps some registers in scratch (values live across
+    a whole work unit), but none of its tile loops -- the backward branches
+    whose body holds at least 64 matrix products and no inner loop of that
+    size -- may read or write scratch."""
+    code = [_code(x) for x in asm]
+    labels = {}
+    for k, x in enumerate(code):
+        m = re.match(r"^(\.LBB\d+_\d+):", x)
+        if m:
+            labels[m.group(1)] = k
+    mfma = [k for k, x in enumerate(code) if x.startswith("v_mfma")]
+    loops = []
+    for k, x in enumerate(code):
+        m = re.search(r"(s_cbranch_\w+|s_branch)\s+(\.LBB\d+_\d+)", x)
+        if m and m.group(2) in labels and labels[m.group(2)] < k:
+            a = labels[m.group(2)]
+            n = sum(1 for y in mfma if a <= y <= k)
+            if 64 <= n <= 120:  # one tile's products (100), not the whole unit loop around it
+                loops.append((a, k))
+    assert loops, "no tile loop found"
+    for a, b in loops:
+        bad = [code[k] for k in range(a, b + 1) if code[k].startswith("scratch_") or
+               (code[k].startswith("buffer_") and "s[0:3]" in code[k])]
+        assert not bad, f"tile loop at lines {a + 1}-{b + 1} touches scratch: {bad[:3]}"
