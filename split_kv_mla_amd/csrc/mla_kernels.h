@@ -1133,38 +1133,35 @@ __device__ __forceinline__ float nan_max(float a, float b) {
   return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
 }
 
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
-  // 256 threads -> one value, broadcast
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float u = __shfl_xor(v, d, 64);
-    v = is_max ? nan_max(v, u) : v + u;
-  }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = is_max ? nan_max(r, red[i]) : r + red[i];
-  return r;
-}
-
-constexpr int kCombineLdsSources = 2048;      // source LSEs staged in LDS
+constexpr int kCombineLdsSources = 2048;  // source LSEs staged in LDS: 8 per thread
+constexpr int kCombineLdsShards = 256;    // per-shard item prefixes staged in LDS
+// Raw buffer resource of a plain byte range (third word of the descriptor on
+// gfx9-family parts: no swizzle, 32-bit data format), and a load offset past
+// any range the combine addresses through one.
+constexpr int32_t kBufferWord3 = 0x00020000;
+constexpr int32_t kBufferPast = 0x7FFFFFF0;
 
 // One workgroup per (request, row, C-column part); its threads form
-// 2048 / C source groups of C / 8 threads, each thread 8 columns.  Few groups
-// suit few sources per row, many groups many (the host picks C).
-template <int C>
+// 2048 / C source groups of C / 8 threads, each thread 8 columns of up to KB
+// sources at a time.  Every load of a phase is issued before the first of
+// them is waited for, so a workgroup makes three dependent trips to memory
+// (the plan, the sources' LSEs and formats, the payloads; the last overlaps
+// the weight reduction) rather than one per source.  A source with LSE -inf
+// adds nothing: its payload is not loaded and never enters a sum.
+template <int C, int KB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  constexpr int kCombineCols = C;
-  constexpr int kCombineGroups = 2048 / C;
-  constexpr int kThreadsPerGroup = C / 8;
+  constexpr int kGroups = 2048 / C;
+  constexpr int kPerGroup = C / 8;
+  constexpr int kLsePerThread = kCombineLdsSources / kThreads;
   __shared__ float src_lse[kCombineLdsSources];
   __shared__ uint8_t src_fmt[kCombineLdsSources];
-  __shared__ f32x4 part[kCombineGroups][kCombineCols / 4];
-  __shared__ float red[8];
+  __shared__ f32x4 part[kGroups][C / 4];
+  __shared__ float red_max[kThreads / 64];
+  __shared__ float red_sum[kThreads / 64];
+  __shared__ int shard_first[kCombineLdsShards + 1];  // items mode: the first item of each shard
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int part_id = blockIdx.x % (kVDim / C);  // which C-column part
   int unit = blockIdx.x / (kVDim / C);
   const int row = unit % p.rows;
@@ -1188,6 +1185,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     const int SC = p.shard_count;
     const int pr0 = b * SC + (p.mode == kMergeShard ? s_out : 0);
     const int pr1 = p.mode == kMergeShard ? pr0 + 1 : (b + 1) * SC;
+    const int32_t L = p.seq_lens[b];  // loaded with the plan entries, not after them
     i0 = p.plan[pr0];
     i1 = p.plan[pr1];   // plan[pairs] is the total item count
     if (i0 < 0 || i1 < i0 || i1 > p.items_cap) {  // a plan that does not fit its slots: report, never read
@@ -1199,7 +1197,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     l_base = (size_t)row * p.items_cap;
     o_stride = (size_t)p.rows * kVDim;
     o_base = (size_t)row * kVDim;
-    const int32_t L = p.seq_lens[b];
     if (L < 0 || L > p.cap_tokens) {
       bad = true;
       fault |= kFaultSeqLen;
@@ -1207,80 +1204,177 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   }
   const int n = i1 - i0;
   const bool staged = n <= kCombineLdsSources;
-  auto lse_of = [&](int i) -> float {  // i relative to i0
-    return staged ? src_lse[i] : p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
-  };
-  auto fmt_at = [&](int i) -> int {  // straight from memory; 0 = fp32 slot
+  // the request's slots addressable with 32-bit buffer offsets
+  const bool buffered = (int64_t)n * (int64_t)o_stride * 4 <= (int64_t)kBufferPast - 4096;
+  auto lse_mem = [&](int i) -> float { return p.src_lse[l_base + (size_t)(i0 + i) * l_stride]; };
+  auto fmt_mem = [&](int i) -> int {  // 0 = fp32 slot
     return p.src_fmt ? p.src_fmt[l_base + (size_t)(i0 + i) * l_stride] : 0;
   };
+  auto lse_of = [&](int i) -> float { return staged ? src_lse[i] : lse_mem(i); };
 
-  // pass 1: stage the source LSEs, their max, and the total weight
+  // pass 1: the sources' LSEs and formats, staged in LDS, and their maximum;
+  // the workgroup that writes the per-shard LSEs also stages the shards'
+  // item prefixes (plan entries b * S .. (b + 1) * S, all inside the plan)
+  const bool shard_lds = p.mode == kCombineItems && part_id == 0 && p.shard_count <= kCombineLdsShards;
+  int first = 0;
+  if (shard_lds && tid <= p.shard_count) first = p.plan[b * p.shard_count + tid];
+  float xs[kLsePerThread];
   float m = -INFINITY;
   int fmt_bits = 0;
-  for (int i = tid; i < n; i += kThreads) {
-    const float x = p.src_lse[l_base + (size_t)(i0 + i) * l_stride];
-    if (x != -INFINITY) fmt_bits |= fmt_at(i);
-    if (staged) {
-      src_lse[i] = x;
-      src_fmt[i] = (uint8_t)fmt_at(i);
-    }
-    m = nan_max(m, x);
-  }
-  // a source whose block-table window named a block outside the cache (its LSE is NaN)
-  if (__any(fmt_bits & 2)) fault |= kFaultBlockId;
-  m = block_reduce(m, true, red);  // its barriers also publish src_lse
-  bad = bad || (m != m);
-  if (p.faults && fault && (threadIdx.x & 63) == 0) atomicOr(p.faults, fault);
-  const bool empty = (m == -INFINITY);
-  float wsum = 0.f;
-  if (!bad && !empty)
-    for (int i = tid; i < n; i += kThreads) {
-      const float x = lse_of(i);
-      if (x != -INFINITY) wsum += __builtin_amdgcn_exp2f((x - m) * kLog2e);
-    }
-  wsum = block_reduce(wsum, false, red);
-
-  // pass 2: weighted sum of this block's 128 columns; thread = (source group, 8 columns)
-  const int sg = tid / kThreadsPerGroup;
-  const int col = part_id * kCombineCols + 8 * (tid % kThreadsPerGroup);
-  f32x4 acc0 = f32x4{}, acc1 = f32x4{};
-  if (!bad && !empty) {
-#pragma unroll 4
-    for (int i = sg; i < n; i += kCombineGroups) {
-      const float x = lse_of(i);
-      if (x == -INFINITY) continue;  // empty source: its payload is never read
-      const float w = __builtin_amdgcn_exp2f((x - m) * kLog2e);
-      const size_t off = o_base + (size_t)(i0 + i) * o_stride + col;  // in floats
-      if ((staged ? src_fmt[i] : fmt_at(i)) & 1) {
-        // an fp16 slot: the same columns in the first half of the slot
-        const f16x8 hv = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.src_o) + 2 * off - col);
+  if (staged) {
+    int fs[kLsePerThread];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc0[e] += w * (float)hv[e];
-          acc1[e] += w * (float)hv[4 + e];
-        }
-      } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.src_o) + off);
-        acc0 += w * src[0];
-        acc1 += w * src[1];
+    for (int k = 0; k < kLsePerThread; ++k) {
+      const int i = tid + k * kThreads;
+      xs[k] = -INFINITY;
+      fs[k] = 0;
+      if (i < n) {
+        xs[k] = lse_mem(i);
+        fs[k] = fmt_mem(i);
       }
     }
+#pragma unroll
+    for (int k = 0; k < kLsePerThread; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < n) {
+        src_lse[i] = xs[k];
+        src_fmt[i] = (uint8_t)fs[k];
+      }
+      if (xs[k] != -INFINITY) fmt_bits |= fs[k];
+      m = nan_max(m, xs[k]);
+    }
+  } else {
+    for (int i = tid; i < n; i += kThreads) {
+      const float x = lse_mem(i);
+      if (x != -INFINITY) fmt_bits |= fmt_mem(i);
+      m = nan_max(m, x);
+    }
   }
-  part[sg][2 * (tid % kThreadsPerGroup)] = acc0;
-  part[sg][2 * (tid % kThreadsPerGroup) + 1] = acc1;
-  __syncthreads();
+  if (shard_lds && tid <= p.shard_count) shard_first[tid] = first;
+  // a source whose block-table window named a block outside the cache (its LSE is NaN)
+  if (__any(fmt_bits & 2)) fault |= kFaultBlockId;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = nan_max(m, __shfl_xor(m, d, 64));
+  if (lane == 0) red_max[wave] = m;
+  __syncthreads();  // also publishes src_lse, src_fmt and shard_first
+  m = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = nan_max(m, red_max[w]);
+  bad = bad || (m != m);
+  if (p.faults && fault && lane == 0) atomicOr(p.faults, fault);
+  const bool empty = (m == -INFINITY);
+  const bool go = !bad && !empty;  // uniform over the workgroup
+
+  // pass 2: the total weight, and the weighted sum of this part's columns;
+  // thread = (source group, 8 columns)
+  const int sg = tid / kPerGroup;
+  const int col = part_id * C + 8 * (tid % kPerGroup);
+  float wsum = 0.f;
+  f32x4 acc0 = f32x4{}, acc1 = f32x4{};
+  // one source's payload, weighted, into the accumulators (r1: fp32 slots only)
+  auto add = [&](float w, bool half, const u32x4& r0, const u32x4& r1) {
+    if (half) {
+      const f16x8 hv = __builtin_bit_cast(f16x8, r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc0[e] += w * (float)hv[e];
+        acc1[e] += w * (float)hv[4 + e];
+      }
+    } else {
+      acc0 += w * __builtin_bit_cast(f32x4, r0);
+      acc1 += w * __builtin_bit_cast(f32x4, r1);
+    }
+  };
+  // address of source i's columns: an fp16 slot holds the row in its first half
+  auto payload = [&](int i, bool half) -> const u32x4* {
+    const size_t slot = o_base + (size_t)(i0 + i) * o_stride;  // in floats: column 0 of the row's slot
+    if (half) return reinterpret_cast<const u32x4*>(reinterpret_cast<const _Float16*>(p.src_o) + 2 * slot + col);
+    return reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(p.src_o) + slot + col);
+  };
+  if (go && staged && buffered) {
+#pragma unroll
+    for (int k = 0; k < kLsePerThread; ++k)
+      if (xs[k] != -INFINITY) wsum += __builtin_amdgcn_exp2f((xs[k] - m) * kLog2e);
+    // Up to KB sources per thread in flight, read from the staged LSEs and
+    // formats with raw buffer loads over this request's slots: a source past
+    // the end, an empty source and the second half of an fp16 slot get an
+    // offset past the buffer's end, which the hardware answers with zeros
+    // and no memory access, so every load is issued back to back without a
+    // branch.
+    const int32_t slot_bytes = (int32_t)(o_stride * 4);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.src_o) + (o_base + (size_t)i0 * o_stride) * 4), 0,
+        n * slot_bytes, kBufferWord3);
+    for (int j0 = sg; j0 < n; j0 += kGroups * KB) {
+      u32x4 r0[KB], r1[KB];
+      float w[KB];
+      bool half[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int i = j0 + k * kGroups;
+        const int ic = min(i, n - 1);
+        const float x = src_lse[ic];
+        half[k] = src_fmt[ic] & 1;
+        const bool live = i < n && x != -INFINITY;
+        w[k] = live ? __builtin_amdgcn_exp2f((x - m) * kLog2e) : 0.f;
+        const int32_t off = ic * slot_bytes + (half[k] ? 2 : 4) * col;
+        r0[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, live ? off : kBufferPast, 0, 0));
+        r1[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, live && !half[k] ? off + 16 : kBufferPast, 0, 0));
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        f32x4 a0, a1;
+        if (half[k]) {
+          const f16x8 hv = __builtin_bit_cast(f16x8, r0[k]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a0[e] = (float)hv[e];
+            a1[e] = (float)hv[4 + e];
+          }
+        } else {
+          a0 = __builtin_bit_cast(f32x4, r0[k]);
+          a1 = __builtin_bit_cast(f32x4, r1[k]);
+        }
+        acc0 += w[k] * a0;  // a skipped source loaded zeros and has weight 0
+        acc1 += w[k] * a1;
+      }
+    }
+  } else if (go) {
+    // more sources than LDS holds: one source at a time, straight from memory
+    for (int i = tid; i < n; i += kThreads) {
+      const float x = lse_mem(i);
+      if (x != -INFINITY) wsum += __builtin_amdgcn_exp2f((x - m) * kLog2e);
+    }
+    for (int i = sg; i < n; i += kGroups) {
+      const float x = lse_mem(i);
+      if (x == -INFINITY) continue;
+      const bool half = fmt_mem(i) & 1;
+      const u32x4* src = payload(i, half);
+      add(__builtin_amdgcn_exp2f((x - m) * kLog2e), half, src[0], half ? u32x4{} : src[1]);
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) wsum += __shfl_xor(wsum, d, 64);
+  if (lane == 0) red_sum[wave] = wsum;
+  part[sg][2 * (tid % kPerGroup)] = acc0;
+  part[sg][2 * (tid % kPerGroup) + 1] = acc1;
+  __syncthreads();  // publishes red_sum and part
+  wsum = red_sum[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) wsum += red_sum[w];
 
   const float qnan = __builtin_nanf("");
   const size_t orow = (size_t)b * p.rows + row;
-  if (tid < kCombineCols / 4) {
+  if (tid < C / 4) {
     f32x4 t = part[0][tid];
 #pragma unroll
-    for (int j = 1; j < kCombineGroups; ++j) t += part[j][tid];
+    for (int j = 1; j < kGroups; ++j) t += part[j][tid];
     const float inv = 1.f / wsum;
     f32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = bad ? qnan : (empty ? 0.f : t[e] * inv);
-    const int c0 = part_id * kCombineCols + 4 * tid;
+    const int c0 = part_id * C + 4 * tid;
     if (p.mode == kMergeShard) {
       float* out = reinterpret_cast<float*>(p.out) + ((size_t)s_out * p.B * p.rows + orow) * kVDim + c0;
       *reinterpret_cast<f32x4*>(out) = o;
@@ -1307,10 +1401,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     return;
   }
   // per-shard LSE over each shard's items: one wavefront per shard
-  const int wave = tid >> 6, lane = tid & 63;
   for (int s = wave; s < p.shard_count; s += kThreads / 64) {
-    const int a0 = p.plan[b * p.shard_count + s] - i0;
-    const int a1 = p.plan[b * p.shard_count + s + 1] - i0;
+    const int a0 = (shard_lds ? shard_first[s] : p.plan[b * p.shard_count + s]) - i0;
+    const int a1 = (shard_lds ? shard_first[s + 1] : p.plan[b * p.shard_count + s + 1]) - i0;
     float ms = -INFINITY;
     for (int i = a0 + lane; i < a1; i += 64) ms = nan_max(ms, lse_of(i));
 #pragma unroll

@@ -140,21 +140,20 @@ int launch_partial(const mla::DecodeParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-// `sources` estimates the sources one output row merges: about 8 per thread
-// of a source group, between 4 groups (C = 512: few sources, fewer and
-// wider workgroups) and 32 (C = 64: hundreds of items of one long request).
+// `sources` estimates the sources one output row merges.  The column part C
+// sets the source groups (2048 / C) and KB the sources one thread keeps in
+// flight.  Measured on the five standard workloads: tens of sources per row
+// run fastest on one workgroup per row (C = 512) with 4 sources in flight,
+// the hundreds of items of one long request on 4 workgroups per row
+// (C = 128) with 8; more loads in flight than that ran slower.
 int launch_combine(const mla::CombineParams& c, int64_t units, int64_t sources, hipStream_t stream) {
-  int groups = 4;
-  while (groups < 32 && groups * 2 * 8 <= sources) groups *= 2;
-  const int C = 2048 / groups;
+  const bool many = sources > 96;
+  const int C = many ? 128 : 512;
   const int64_t blocks = units * (mla::kVDim / C);
   if (blocks > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  switch (C) {
-    case 512: hipLaunchKernelGGL(mla::combine_kernel<512>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
-    case 256: hipLaunchKernelGGL(mla::combine_kernel<256>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
-    case 128: hipLaunchKernelGGL(mla::combine_kernel<128>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
-    default: hipLaunchKernelGGL(mla::combine_kernel<64>, dim3((int)blocks), dim3(mla::kThreads), 0, stream, c); break;
-  }
+  const dim3 grid((int)blocks), block(mla::kThreads);
+  if (many) hipLaunchKernelGGL((mla::combine_kernel<128, 8>), grid, block, 0, stream, c);
+  else hipLaunchKernelGGL((mla::combine_kernel<512, 4>), grid, block, 0, stream, c);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
