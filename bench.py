@@ -65,6 +65,8 @@ def parse():
                     help="skip the fp8 KV-cache variant of the workload")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the timing of the chunked-context KV gather")
+    ap.add_argument("--no-single-p", action="store_true",
+                    help="skip the single-rounding P mode of the workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -79,8 +81,9 @@ def parse():
 
 KERNEL_SOURCES = ("split_kv_mla_amd/csrc/mla_kernels.h", "split_kv_mla_amd/csrc/mla_plan.h",
                   "split_kv_mla_amd/csrc/mla_split_kv.hip")
-PARTIAL_KERNEL = "mla::partial_kernel<false>"      # the bf16 cache's instantiation
-PARTIAL_KERNEL_FP8 = "mla::partial_kernel<true>"   # the fp8 cache's
+PARTIAL_KERNEL = "mla::partial_kernel<false, true>"      # the bf16 cache's instantiation (P as hi + lo)
+PARTIAL_KERNEL_FP8 = "mla::partial_kernel<true, true>"   # the fp8 cache's
+PARTIAL_KERNEL_SINGLE_P = "mla::partial_kernel<false, false>"  # bf16 cache, P rounded once
 
 
 def kernel_source_sha():
@@ -242,23 +245,33 @@ def merge_leg(mla, dev, launches):
             "frac": gbps / HBM_PEAK_GBPS}
 
 
-def fp8_leg(mla, dev, launches, min_set_mb, counters_workload):
-    """The same long-context workload with its cache stored as fp8 E4M3 codes
-    plus one float32 scale per token (580 bytes per token instead of 1152):
-    the partial kernel's own duration (HIP events the library records on its
-    stream, cycling cache copies past the Infinity Cache), and the whole step
+def variant_leg(mla, dev, launches, min_set_mb, counters_workload, fp8=False, single_p=False):
+    """A variant of the long-context workload: its cache stored as fp8 E4M3
+    codes plus one float32 scale per token (580 bytes per token instead of
+    1152), or P rounded once to bf16 (half the value products): the partial
+    kernel's own duration (HIP events the library records on its stream,
+    cycling cache copies past the Infinity Cache), and the whole step
     (back-to-back steps between two events)."""
     import torch
     import workloads
-    w = workloads.to_fp8(workloads.long_context(1))
+    w = workloads.long_context(1)
+    if fp8:
+        w = workloads.to_fp8(w)
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)
-    kv_mb = (w.kv_bits.nbytes + w.kv_scale.nbytes) / 1e6
+    if fp8:
+        kv_mb = (w.kv_bits.nbytes + w.kv_scale.nbytes) / 1e6
+    else:
+        kv_mb = w.kv_bits.nbytes / 1e6
     copies = max(1, math.ceil(min_set_mb / kv_mb))
-    kvs = [(torch.from_numpy(w.kv_bits).to(dev), torch.from_numpy(w.kv_scale).to(dev)) for _ in range(copies)]
+    if fp8:
+        kvs = [(torch.from_numpy(w.kv_bits).to(dev), torch.from_numpy(w.kv_scale).to(dev)) for _ in range(copies)]
+    else:
+        host = torch.from_numpy(w.kv_bits.view(np.int16)).view(torch.bfloat16)
+        kvs = [(host.to(dev), None) for _ in range(copies)]
     S, I = w.num_shards, w.interleave
-    a = mla.decode_args(q, kvs[0][0], bt, sl, S, I, w.scale, w.causal, kv_scale=kvs[0][1])
+    a = mla.decode_args(q, kvs[0][0], bt, sl, S, I, w.scale, w.causal, kv_scale=kvs[0][1], single_p=single_p)
     ws = mla.new_workspace(a, dev)
     out = torch.empty((w.B, w.R, w.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((S, w.B, w.R, w.H), dtype=torch.float32, device=dev)
@@ -267,7 +280,7 @@ def fp8_leg(mla, dev, launches, min_set_mb, counters_workload):
     def step(i, events=None):
         kv, ks = kvs[i % copies]
         mla.mla_split_decode(q, kv, bt, sl, S, I, w.scale, w.causal, out=out, lse=lse, lse_final=lf,
-                             workspace=ws, events=events, kv_scale=ks)
+                             workspace=ws, events=events, kv_scale=ks, single_p=single_p)
 
     for i in range(3):
         step(i)
@@ -290,15 +303,19 @@ def fp8_leg(mla, dev, launches, min_set_mb, counters_workload):
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / launches
     tokens = int(w.seq_lens.astype(np.int64).sum())
-    kb = tokens * (576 + 4) + w.B * w.R * w.H * ROW_BYTES  # what the partial kernel must read: codes, scales, q
+    row = 576 + 4 if fp8 else ROW_BYTES
+    kb = tokens * row + w.B * w.R * w.H * ROW_BYTES  # what the partial kernel must read: the cache rows and q
     gbps = kb / (part / 1e3) / 1e9
-    return {"workload": w.name, "kv_bytes_per_token": 580, "kv_copies_cycled": copies,
-            "partial_kernel_ms": part, "combine_kernel_ms": comb, "ms_per_step": step_ms,
-            "value": tokens / (step_ms / 1e3), "unit": "KV tokens/s",
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "kernel": PARTIAL_KERNEL_FP8,
-                         "bytes_per_launch": kb,
-                         "traffic": load_traffic(counters_workload, PARTIAL_KERNEL_FP8)}}
+    kernel = PARTIAL_KERNEL_FP8 if fp8 else (PARTIAL_KERNEL_SINGLE_P if single_p else PARTIAL_KERNEL)
+    rec = {"workload": w.name, "kv_bytes_per_token": row, "kv_copies_cycled": copies,
+           "partial_kernel_ms": part, "combine_kernel_ms": comb, "ms_per_step": step_ms,
+           "value": tokens / (step_ms / 1e3), "unit": "KV tokens/s",
+           "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": gbps / HBM_PEAK_GBPS, "kernel": kernel, "bytes_per_launch": kb,
+                        "traffic": load_traffic(counters_workload, kernel)}}
+    if single_p:
+        rec["p_precision"] = "bf16 (one rounding)"
+    return rec
 
 
 def gather_leg(mla, dev, steps):
@@ -461,7 +478,9 @@ def main():
     # the chunked-context KV gather (the prefill side of the same shards)
     gather = None if args.no_gather else gather_leg(mla, dev, args.event_steps)
     # the same decode over an fp8 cache
-    fp8 = None if args.no_fp8 else fp8_leg(mla, dev, args.event_steps, args.min_kv_set_mb, w.name)
+    fp8 = None if args.no_fp8 else variant_leg(mla, dev, args.event_steps, args.min_kv_set_mb, w.name, fp8=True)
+    single = None if args.no_single_p else variant_leg(mla, dev, args.event_steps, args.min_kv_set_mb, w.name,
+                                                       single_p=True)
 
     # K steps in one graph, replayed between synchronisations
     K = args.steps
@@ -532,6 +551,8 @@ def main():
         rec["context_gather"] = gather
     if fp8 is not None:
         rec["fp8_kv"] = fp8
+    if single is not None:
+        rec["single_p"] = single
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -81,6 +81,22 @@ enum {
                        /* float32 scale per token in kv_scale: value = code * scale      */
 };
 
+/* How the softmax weights P enter the bf16 value products
+ * (mla_decode_args.p_precision).  The pages fix no precision for P; the
+ * value product is a bf16 matrix product, so P is rounded to bf16 on the way
+ * in.  Rounded once, each weight moves by up to 2^-9 of itself: on rows whose
+ * output is a near-cancelling mix of large values (the padded workload's x30
+ * outliers) that exceeds |err| <= 2e-3 + 1e-2 |ref| several times over, so
+ * the default splits P into two bf16 terms (residual <= 2^-16 of P) at the
+ * cost of twice the value products.  MLA_P_BF16 asks for the single rounding:
+ * 10-20 % faster, for callers whose rows are well conditioned (long, flat
+ * softmaxes: the 120k-token request stays at 0.21 of the tolerance; the
+ * sharper verification rows already put 14 of 4.2 M outputs past it). */
+enum {
+  MLA_P_SPLIT = 0,  /* P = P_hi + P_lo, both bf16 (the default)                   */
+  MLA_P_BF16 = 1    /* P rounded once to bf16                                     */
+};
+
 /* Device scratch bytes behind mla_split_decode_static (96 MiB per GPU). */
 #define MLA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
 
@@ -115,6 +131,7 @@ typedef struct mla_decode_args {
                               /* kv_cache holds uint8 codes [num_blocks, block_size, 576] */
   const float* kv_scale;      /* fp8 only: device float32 [num_blocks, block_size], the   */
                               /* scale of each token's whole row; ignored for bf16        */
+  int32_t p_precision;        /* MLA_P_SPLIT (0, the default) or MLA_P_BF16               */
 } mla_decode_args;
 
 /* Bytes of device workspace the two decode entry points need for `a`

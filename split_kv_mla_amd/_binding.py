@@ -39,6 +39,7 @@ class MlaDecodeArgs(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("kv_format", ctypes.c_int32),
         ("kv_scale", ctypes.c_void_p),
+        ("p_precision", ctypes.c_int32),
     ]
 
 
@@ -145,14 +146,17 @@ def _stream(device):
 
 
 KV_BF16, KV_FP8_E4M3 = 0, 1
+P_SPLIT, P_BF16 = 0, 1  # P as bf16 hi + lo (default), or rounded once to bf16
 
 
 def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal=True,
-                kv_scale=None):
+                kv_scale=None, single_p=False):
     """Validate the decode inputs and build the C argument struct.
 
     kv_cache is bf16, or fp8 E4M3 codes (torch.float8_e4m3fn or uint8) with
-    ``kv_scale`` float32 [num_blocks, block_size], one scale per token."""
+    ``kv_scale`` float32 [num_blocks, block_size], one scale per token.
+    ``single_p``: round the softmax weights once to bf16 (P_BF16) instead of
+    splitting them into two bf16 terms."""
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
         raise ValueError("q must be [B, R, H, 576]")
     B, R, H, _ = q.shape
@@ -185,6 +189,7 @@ def decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, soft
     a.causal = 1 if causal else 0
     a.kv_format = KV_FP8_E4M3 if fp8 else KV_BF16
     a.kv_scale = kv_scale.data_ptr() if fp8 else None
+    a.p_precision = P_BF16 if single_p else P_SPLIT
     return a
 
 
@@ -221,17 +226,18 @@ def new_workspace(args: MlaDecodeArgs, device):
 
 def mla_split_decode(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
                      causal=True, out=None, lse=None, lse_final=None, workspace=None,
-                     want_lse_final=True, events=None, kv_scale=None):
+                     want_lse_final=True, events=None, kv_scale=None, single_p=False):
     """Split-KV decode of every shard plus the LSE combine.
 
     ``events``: optional (begin, mid, end) torch.cuda.Event objects, already
     recorded once, that the library records around its partial and combine
     kernels (calls mla_split_decode_timed).
     ``kv_scale``: the per-token scales of an fp8 cache.
+    ``single_p``: P rounded once to bf16 (faster; see P_BF16 in the C header).
     Returns (out bf16 [B,R,H,512], lse fp32 [S,B,R,H], lse_final fp32 [B,R,H] or None).
     """
     a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
-                    kv_scale)
+                    kv_scale, single_p)
     B, R, H, _ = q.shape
     dev = q.device
     if out is None:
@@ -262,12 +268,12 @@ STATIC_SCRATCH_BYTES = 96 << 20
 
 
 def mla_split_decode_static(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
-                            out, lse, lse_final=None, causal=True, kv_scale=None):
+                            out, lse, lse_final=None, causal=True, kv_scale=None, single_p=False):
     """mla_split_decode into caller-given outputs, with the library's static
     device scratch as workspace: neither the library nor this binding
     allocates device memory.  Calls that overlap on one GPU race."""
     a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
-                    kv_scale)
+                    kv_scale, single_p)
     B, R, H, _ = q.shape
     dev = q.device
     _need(out, "out", torch.bfloat16, (B, R, H, V_DIM), dev)
@@ -281,13 +287,13 @@ def mla_split_decode_static(q, kv_cache, block_table, seq_lens, num_shards, inte
 
 def mla_shard_decode_partial(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale,
                              causal=True, shard_begin=0, shard_count=None, out_partial=None, lse=None,
-                             workspace=None, kv_scale=None):
+                             workspace=None, kv_scale=None, single_p=False):
     """Partial attention of shards [shard_begin, shard_begin + shard_count).
 
     Returns (out_partial fp32 [shard_count,B,R,H,512], lse fp32 [shard_count,B,R,H]).
     """
     a = decode_args(q, kv_cache, block_table, seq_lens, num_shards, interleave, softmax_scale, causal,
-                    kv_scale)
+                    kv_scale, single_p)
     B, R, H, _ = q.shape
     dev = q.device
     sc = num_shards - shard_begin if shard_count is None else shard_count

@@ -493,7 +493,9 @@ __device__ __forceinline__ void copy_q_rows(const DecodeParams& p, int b, int ro
 
 // ------------------------------------------------------------ partial kernel
 
-template <bool kFp8>
+// kLo: P enters the value products as bf16 hi + lo (the default); without
+// it, as one bf16 rounding per weight (half the value products).
+template <bool kFp8, bool kLo>
 __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
   // LDS bytes of one ring stage, and LDS-DMA loads per wavefront per tile
   constexpr int kStageBytes = kFp8 ? kTile8Bytes : kTileBytes;
@@ -832,7 +834,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // Half kb of the tile's P^T fragments (tokens 16*kb + ...).  P = P_hi +
       // P_lo, both bf16: a single bf16 P would cost up to 2^-8 of relative
       // weight per token, too much for rows of a few tokens or with outlier
-      // values; the pair leaves a residual of at most 2^-16 p.
+      // values; the pair leaves a residual of at most 2^-16 p.  Without kLo
+      // only P_hi is formed and used.
       // fp8: the V weight of a token is its softmax numerator times its scale.
       auto make_p = [&](PFrag& pf, const f32x16& sc, float msafe, int kb, const f32x16& ks) {
 #pragma unroll
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           if constexpr (kFp8) x *= ks[8 * kb + j];
           const __bf16 hi = (__bf16)x;
           pf.hi[kb][j] = hi;
-          pf.lo[kb][j] = (__bf16)(x - (float)hi);
+          if constexpr (kLo) pf.lo[kb][j] = (__bf16)(x - (float)hi);
         }
       };
       // S^T of the tile in `buf` on its own (the first tile of the walk).
@@ -873,9 +876,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         return sc;
       };
       // PV product i of a tile (64 per tile): fragment i/2 (vcur: converted at
-      // the even product), P_hi for even i, P_lo for odd.
+      // the even product), P_hi for even i, P_lo for odd (skipped without kLo;
+      // the schedule of reads stays the same).
       auto pv_mfma = [&](const VRaw* vf, bf16x8& vcur, const PFrag& pf, int i) {
         const int f = i >> 1, kb = f >> 4, db = f & 15;
+        if constexpr (!kLo) {
+          if (i & 1) return;
+        }
         if constexpr (kFp8) {
           if (!(i & 1)) vcur = k_val(vf[f]);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, (i & 1) ? pf.lo[kb] : pf.hi[kb], acc[db], 0, 0, 0);

@@ -38,6 +38,7 @@ int check_args(const mla_decode_args* a) {
   if (a->batch > 0 && (!a->q || !a->kv_cache || !a->block_table || !a->seq_lens)) return MLA_ERR_INVALID_ARG;
   if (a->kv_format != MLA_KV_BF16 && a->kv_format != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
   if (a->kv_format == MLA_KV_FP8_E4M3 && a->batch > 0 && !a->kv_scale) return MLA_ERR_INVALID_ARG;
+  if (a->p_precision != MLA_P_SPLIT && a->p_precision != MLA_P_BF16) return MLA_ERR_INVALID_ARG;
   if (a->rows > 8 || (int64_t)a->rows * a->heads > 1024) return MLA_ERR_UNSUPPORTED;
   const int lg = ilog2_exact(a->block_size);
   if (lg < 0 || a->block_size > 1024) return MLA_ERR_UNSUPPORTED;
@@ -131,12 +132,16 @@ mla::DecodeParams decode_params(const mla_decode_args* a, const Plan& pl, int32_
   return p;
 }
 
-int launch_partial(const mla::DecodeParams& p, hipStream_t stream) {
+int launch_partial(const mla::DecodeParams& p, bool single_p, hipStream_t stream) {
   // persistent: one workgroup per compute unit walks all (item, row group) units
-  if (p.kv_scale)
-    hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mla::partial_kernel<false>, dim3(mla::kNumCUs), dim3(mla::kThreads), 0, stream, p);
+  const dim3 grid(mla::kNumCUs), block(mla::kThreads);
+  if (p.kv_scale) {
+    if (single_p) hipLaunchKernelGGL((mla::partial_kernel<true, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla::partial_kernel<true, true>), grid, block, 0, stream, p);
+  } else {
+    if (single_p) hipLaunchKernelGGL((mla::partial_kernel<false, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla::partial_kernel<false, true>), grid, block, 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -211,7 +216,7 @@ int mla_shard_decode_partial(const mla_decode_args* a, int32_t shard_begin, int3
   if (workspace_bytes < pl.total()) return MLA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, shard_begin, shard_count, workspace);
-  if ((st = launch_partial(p, s)) != MLA_OK) return st;
+  if ((st = launch_partial(p, a->p_precision == MLA_P_BF16, s)) != MLA_OK) return st;
   mla::CombineParams c{};
   c.src_o = p.part_o;
   c.src_lse = p.part_lse;
@@ -267,7 +272,7 @@ int mla_split_decode_timed(const mla_decode_args* a, void* out, float* lse, floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::DecodeParams p = decode_params(a, pl, 0, a->num_shards, workspace);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return MLA_ERR_HIP;
-  if ((st = launch_partial(p, s)) != MLA_OK) return st;
+  if ((st = launch_partial(p, a->p_precision == MLA_P_BF16, s)) != MLA_OK) return st;
   if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), s) != hipSuccess) return MLA_ERR_HIP;
   mla::CombineParams c{};
   c.src_o = p.part_o;

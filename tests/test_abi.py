@@ -371,6 +371,20 @@ def test_fp8_cache_needs_its_scales():
     assert lib.mla_workspace_bytes(ctypes.byref(a)) > 0
 
 
+def test_p_precision_is_split_or_single_bf16():
+    lib = m.load_library()
+    null = ctypes.c_void_p(0)
+    a = _args()
+    assert a.p_precision == _binding.P_SPLIT
+    a.p_precision = _binding.P_BF16
+    assert lib.mla_workspace_bytes(ctypes.byref(a)) > 0
+    for bad in (2, -1):
+        a.p_precision = bad
+        assert lib.mla_workspace_bytes(ctypes.byref(a)) == 0
+        assert lib.mla_split_decode(ctypes.byref(a), ctypes.c_void_p(8), ctypes.c_void_p(8), null,
+                                    ctypes.c_void_p(8), 1 << 40, null) == -1
+
+
 def test_static_entry_rejects_calls_beyond_its_scratch_without_launching():
     lib = m.load_library()
     vp = ctypes.c_void_p
