@@ -240,6 +240,58 @@ def test_lse_combine_skips_empty_sources():
     assert np.all(out[2] == 0.0) and not np.signbit(out[2]).any()
 
 
+def _combine_inputs(S, lead, seed, device, empty_frac=0.3):
+    """Caller partials on the device: fp32 N(0, 1) payloads, LSEs uniform in
+    [-6, 6] with a fraction set to -inf (their payloads NaN), and the first
+    row of every source empty."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    po = torch.randn((S,) + lead + (512,), generator=g, device=device, dtype=torch.float32)
+    lp = torch.rand((S,) + lead, generator=g, device=device, dtype=torch.float32) * 12 - 6
+    empty = torch.rand((S,) + lead, generator=g, device=device) < empty_frac
+    flat = empty.view(S, -1)
+    flat[:, 0] = True
+    lp[empty] = -float("inf")
+    po[empty] = float("nan")
+    return po, lp
+
+
+def test_lse_combine_rows_of_many_sources():
+    """2 100 sources per row: more than the combine stages in LDS, so it takes
+    its one-source-at-a-time path."""
+    m = _lib()
+    S, lead = 2100, (2, 1, 4)
+    po, lp = _combine_inputs(S, lead, 41, "cuda:0")
+    _say(f"[parity] lse_combine over {S} sources per row")
+    out, lf = m.mla_lse_combine(po, lp)
+    torch.cuda.synchronize()
+    eo, el = oracle.lse_combine_oracle(po.cpu().numpy(), lp.cpu().numpy())
+    assert_out_close(bf16_to_f64(out), eo, what="many-source combine out")
+    assert_lse_close(lf.cpu().double().numpy(), el, what="many-source combine lse")
+    o0 = bf16_to_f64(out)[0, 0, 0]
+    assert np.all(o0 == 0.0) and not np.signbit(o0).any()
+
+
+def test_lse_combine_sources_past_32_bit_offsets():
+    """6 sources of 180 000 rows each: one row's sources span more than 2^31
+    bytes, past what the combine addresses with 32-bit buffer offsets, so it
+    reads them one at a time.  Sampled rows against the oracle."""
+    m = _lib()
+    S, lead = 6, (1, 1, 180000)
+    po, lp = _combine_inputs(S, lead, 42, "cuda:0")
+    _say(f"[parity] lse_combine over {S} sources of {lead[2]} rows ({po.numel() * 4 / 2**30:.1f} GiB)")
+    out, lf = m.mla_lse_combine(po, lp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(42)
+    rows = np.unique(np.concatenate([[0, 1, lead[2] // 2, lead[2] - 1], rng.integers(0, lead[2], 60)]))
+    idx = torch.from_numpy(rows).cuda()
+    eo, el = oracle.lse_combine_oracle(po[:, 0, 0, idx].cpu().numpy(), lp[:, 0, 0, idx].cpu().numpy())
+    assert_out_close(bf16_to_f64(out[0, 0, idx]), eo, what="large combine out")
+    assert_lse_close(lf[0, 0, idx].cpu().double().numpy(), el, what="large combine lse")
+    del po, lp
+    torch.cuda.empty_cache()
+
+
 def test_repeat_runs_bitwise_identical():
     w = build("det", [3000, 700], R=1, H=128, num_shards=8, interleave=1, seed=33)
     a = _run_split(w)
