@@ -110,13 +110,17 @@ struct DecodeParams {
 
 // ---------------------------------------------------------------- helpers
 
+// Inclusive prefix sum over the wavefront with DPP moves (no lane-address
+// registers to keep, unlike shuffles through LDS): shifts by 1, 2, 4 and 8
+// inside each 16-lane row (a lane with no source adds 0), then lane 15's sum
+// into rows 1 and 3 and lane 31's into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 
@@ -124,7 +128,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 template <int NT = kThreads>
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
   const int incl = wave_incl_scan(v);
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: no per-lane slot address
   if ((threadIdx.x & 63) == 63) scratch[w] = incl;
   __syncthreads();
   int off = 0, tot = 0;
@@ -152,7 +156,7 @@ __device__ __forceinline__ bool block_any(bool v, int* slots, int wave, int lane
   int o = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) o |= slots[i];
-  const bool r = o != 0;
+  const bool r = __builtin_amdgcn_readfirstlane(o) != 0;  // the same in every lane: a scalar
   __syncthreads();  // the slots can be reused after this
   return r;
 }
@@ -177,12 +181,18 @@ __device__ __forceinline__ int32_t pair_tiles(const DecodeParams& p, int pr) {
   return pair_tiles_of(p, pr, pair_len(p, pr));
 }
 
+// The value of lane l ^ 32 (the other half of the wavefront) for the caller's
+// lane index l: one LDS permute, addressed from the caller's lane so that no
+// address register is shared (and kept live) between call sites.
+__device__ __forceinline__ float other_half(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+}
+
 template <int NT = kThreads>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  v = __builtin_amdgcn_readlane(wave_incl_scan(v), 63);  // the wavefront's total
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) scratch[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)] = v;
   __syncthreads();
   int t = 0;
 #pragma unroll
@@ -225,14 +235,14 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
       const int t = lane < P ? pair_tiles_of(p, lane, L) : 0;
       const int cost = pair_cost(t);
       const int cinc = wave_incl_scan(cost);
-      const int T = __shfl(cinc, 63, 64);
+      const int T = __builtin_amdgcn_readlane(cinc, 63);
       const int wmin = max(1, ceil_div(T, p.slots));
       const int m = ceil_div(wmin, p.tpi_max);
       const int U = ceil_div(wmin, m);
       const int cex = cinc - cost;
       const int items = pair_items(cex + kPieceCost, t, U);
       const int iinc = wave_incl_scan(items);
-      const int ntot = __shfl(iinc, 63, 64);
+      const int ntot = __builtin_amdgcn_readlane(iinc, 63);
       if (lane < P) {
         cstart[lane] = cex;
         starts[lane] = iinc - items;
@@ -251,8 +261,10 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
       }
     }
     __syncthreads();
-    const int U = scratch[4];
-    return Plan{U, scratch[5] * U, cstart[P], starts[P]};
+    // the plan is the same in every lane: scalar registers
+    const int U = __builtin_amdgcn_readfirstlane(scratch[4]);
+    return Plan{U, __builtin_amdgcn_readfirstlane(scratch[5]) * U, __builtin_amdgcn_readfirstlane(cstart[P]),
+                __builtin_amdgcn_readfirstlane(starts[P])};
   }
   const bool in_reg = P <= NT;
   const int my_t = (in_reg && (int)threadIdx.x < P) ? pair_tiles(p, threadIdx.x) : 0;
@@ -301,7 +313,8 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
     }
   }
   __syncthreads();
-  return Plan{U, m * U, T, irun};
+  return Plan{__builtin_amdgcn_readfirstlane(U), __builtin_amdgcn_readfirstlane(m * U), __builtin_amdgcn_readfirstlane(T),
+              __builtin_amdgcn_readfirstlane(irun)};
 }
 
 struct PairAt {
@@ -317,12 +330,15 @@ __device__ PairAt pair_at(const DecodeParams& p, const Plan& pl, int x, const in
                           int* scratch) {
   const int P = p.pairs;
   if (P <= kPlanPairsLds) {
-    int lo = 0, hi = P;  // largest pr with cstart[pr] <= x: empty pairs share the next one's start
+    // largest pr with cstart[pr] <= x (empty pairs share the next one's
+    // start); x and the prefixes are the same in every lane: scalar registers
+    int lo = 0, hi = P;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (cstart[mid] <= x) lo = mid; else hi = mid;
+      if (__builtin_amdgcn_readfirstlane(cstart[mid]) <= x) lo = mid; else hi = mid;
     }
-    return PairAt{lo, cstart[lo], cstart[lo + 1], starts[lo]};
+    return PairAt{lo, __builtin_amdgcn_readfirstlane(cstart[lo]), __builtin_amdgcn_readfirstlane(cstart[lo + 1]),
+                  __builtin_amdgcn_readfirstlane(starts[lo])};
   }
   // many pairs: scan the prefixes again
   int crun = 0, irun = 0;
@@ -344,7 +360,8 @@ __device__ PairAt pair_at(const DecodeParams& p, const Plan& pl, int x, const in
     irun += itot;
   }
   __syncthreads();
-  return PairAt{scratch[8], scratch[9], scratch[10], scratch[11]};
+  return PairAt{__builtin_amdgcn_readfirstlane(scratch[8]), __builtin_amdgcn_readfirstlane(scratch[9]),
+                __builtin_amdgcn_readfirstlane(scratch[10]), __builtin_amdgcn_readfirstlane(scratch[11])};
 }
 
 // XOR key of token tau's 16-byte pieces inside each 128-byte group of its LDS
@@ -605,7 +622,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     // Query rows of this wavefront: row = r * H + h, 32 per wavefront.
     const int row = rg * kRowsPerGroup + wave * kRowsPerWave + l32;
     const bool row_ok = row < p.rows_total;
-    const int r = row_ok ? row / p.H : 0;
+    int H = p.H;  // opaque: the division's reciprocal is formed per unit, not kept live
+    asm volatile("" : "+s"(H));
+    const int r = row_ok ? row / H : 0;
     // Local tokens the row sees, cut at the item's end: the walk also scores the
     // stage after the item's last tile, and this masks all of it.
     const int lim = min(local_len(row_ok ? row_len(L, p.R, r, p.causal) : 0, S, I, s), tile1 * kTile);
@@ -720,6 +739,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     };
     auto walk = [&](auto max_only_tag, bool prologue_issued, bool& overflow) {
       constexpr bool kMaxOnly = decltype(max_only_tag)::value;
+      // The item's first tile through an opaque copy: the slow-path walks
+      // recompute their first tiles' addresses instead of sharing the main
+      // walk's, which would keep those live (and spilled) across it.
+      int t0 = tile0;
+      asm volatile("" : "+s"(t0));
       // LDS read offsets of this lane (from an opaque lane copy: recomputing
       // them per walk beats keeping them live through the prologue)
       int lane_r = lane;
@@ -795,14 +819,14 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // tiles kept in flight ahead of the tile being consumed
       constexpr int kAheadTiles = kMaxOnly ? kStages - 1 : kLead;
       if (!prologue_issued) {
-        for (int k = 0; k < kAheadTiles; ++k) issue_tile(tile0 + k, k);
+        for (int k = 0; k < kAheadTiles; ++k) issue_tile(t0 + k, k);
       } else {
         // the prologue issued tile 0 alone: the rest of the lead follows it
         static_assert(kLead == 2, "the prologue's first tile plus one");
         wait_vmcnt<0>();
-        issue_tile(tile0 + 1, 1);
+        issue_tile(t0 + 1, 1);
       }
-      auto next_src = tile_src(tile0 + kAheadTiles);
+      auto next_src = tile_src(t0 + kAheadTiles);
       float m_walk = -INFINITY;
 
       // Scores of item tile kt (lane: row l32, tokens 8*(i/4) + 4*g + (i%4)):
@@ -810,7 +834,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       // reference, or (kMaxOnly) folds the row maximum into m_walk.
       // Branch-free, so that it schedules among the matrix products.
       auto prep = [&](f32x16& sc, int kt, const f32x16& ks) -> float {
-        const int jt = (tile0 + kt) * kTile + 4 * g;
+        const int jt = (t0 + kt) * kTile + 4 * g;
         if constexpr (kFp8) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[i] *= ks[i];
@@ -820,7 +844,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         float mx = sc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+        mx = fmaxf(mx, other_half(mx, lane_r)) * c;
         if constexpr (kMaxOnly) {
           m_walk = fmaxf(m_walk, mx);
           return 0.f;
@@ -904,7 +928,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           // slow-path walk keeps kStages - 1 tiles in flight)
           lds_barrier();
           if (k + kStages - 1 < nt) issue_src(next_src, (k + kStages - 1) % kStages);
-          next_src = tile_src(tile0 + k + kStages);  // clamped past the end: harmless
+          next_src = tile_src(t0 + k + kStages);  // clamped past the end: harmless
           const char* buf = ring + (k % kStages) * kStageBytes;
           f32x16 sc = qk_alone(buf);
           prep(sc, k, tile_scales(buf));
@@ -940,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           // stage of tile k + kLead - kStages takes tile k + kLead
           lds_barrier();
           if (k + kLead < nt) issue_src(next_src, (k + kLead) % kStages);
-          next_src = tile_src(tile0 + k + kLead + 1);  // clamped past the end: harmless
+          next_src = tile_src(t0 + k + kLead + 1);  // clamped past the end: harmless
           const char* buf = ring + (k % kStages) * kStageBytes;
           const char* nbuf = ring + ((k + 1) % kStages) * kStageBytes;
           // O^T[dim][row] += V^T[dim][token] P^T[token][row]: product i uses
@@ -1022,24 +1046,22 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
       __syncthreads();  // every wavefront is done with the ring before it stages rows
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const size_t lrow = (size_t)row * p.items_cap + item;  // the row's LSE and format of this item
+    // The epilogue's lane values come from a fresh opaque copy of the thread
+    // id rather than from before the walk, so that none stays live across it.
+    int tid_e = threadIdx.x;
+    asm volatile("" : "+v"(tid_e));
+    const int e_lane = tid_e & 63;
+    const int e_g = e_lane >> 5;
+    const int e_l32 = e_lane & 31;
+    const int e_row = rg * kRowsPerGroup + wave * kRowsPerWave + e_l32;
+    const bool e_row_ok = e_row < p.rows_total;
+    const float l_tot = l_run + other_half(l_run, e_lane);
+    const size_t lrow = (size_t)e_row * p.items_cap + item;  // the row's LSE and format of this item
     float lse = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (bad) lse = __builtin_nanf("");
-    if (row_ok && g == 0) p.part_lse[lrow] = lse;
-    const bool live = row_ok && l_tot > 0.f;
+    if (e_row_ok && e_g == 0) p.part_lse[lrow] = lse;
+    const bool live = e_row_ok && l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
-    // The row's largest |o| picks its storage: fp16 when it is at most
-    // kHalfPartialMax (rounding then moves no element by more than 2^-10, half
-    // the output's absolute tolerance, whatever the merge weights), else fp32.
-    float amax = 0.f;
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
-    const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
-    if (row_ok && g == 0 && (live || bad)) p.part_fmt[lrow] = bad ? 2 : (as_half ? 1 : 0);
     // lane holds columns 32*db + 8*q + 4*g + (0..3) in acc[db][4q .. 4q+3].
     // Rows leave through the idle ring, transposed so that a store writes a
     // whole 1 KiB piece of a row (the scattered pieces of the register layout
@@ -1050,22 +1072,60 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
     static_assert(16 * kStride32 <= kRowsPerWave * kStride, "fp32 half of the rows fits the region");
     char* stage = ring + wave * (kRowsPerWave * kStride);
     const size_t prow0 = (size_t)item * p.rows_total + rg * kRowsPerGroup + wave * kRowsPerWave;
-    // fp32 rows: 16 rows of the wavefront at a time, each row two 1 KiB stores
-    const uint64_t f32_rows = __ballot(live && !as_half && g == 0);  // bit r: row l32 = r
+    // Every row is staged as fp16, and the row's largest |o| is taken in the
+    // same pass (each accumulator is read once on the common path).  It picks
+    // the row's storage: fp16 when it is at most kHalfPartialMax (rounding then
+    // moves no element by more than 2^-10, half the output's absolute
+    // tolerance, whatever the merge weights), else fp32.
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[db][4 * q + e];
+          amax = fmaxf(amax, fabsf(x));
+          v[e] = (_Float16)(x * inv);
+        }
+        *reinterpret_cast<f16x4*>(stage + e_l32 * kStride + 2 * (32 * db + 8 * q + 4 * e_g)) = v;
+      }
+    amax = fmaxf(amax, other_half(amax, e_lane)) * inv;
+    const bool as_half = live && amax <= kHalfPartialMax;  // NaN stays fp32
+    if (e_row_ok && e_g == 0 && (live || bad)) p.part_fmt[lrow] = bad ? 2 : (as_half ? 1 : 0);
+    // fp16 rows: the whole wavefront's 32 rows at once
+    {
+      asm volatile("" ::: "memory");  // the reads below see every lane's writes
+      const uint64_t half_rows = __ballot(as_half && e_g == 0);  // bit r: row l32 = r
+      _Float16* po = reinterpret_cast<_Float16*>(p.part_o) + prow0 * (2 * kVDim) + 8 * e_lane;
+#pragma unroll 4
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride + 16 * e_lane);
+        if ((half_rows >> r) & 1) store_through(po + (size_t)r * (2 * kVDim), v);
+      }
+      asm volatile("" ::: "memory");  // read before the fp32 rows overwrite the region
+    }
+    // fp32 rows (rare): 16 rows of the wavefront at a time, each row two 1 KiB
+    // stores.  The scale goes through an opaque copy, so that these products
+    // are formed here and not kept from the pass above.
+    const uint64_t f32_rows = __ballot(live && !as_half && e_g == 0);  // bit r: row l32 = r
     if (f32_rows) {
-      float* po = reinterpret_cast<float*>(p.part_o) + prow0 * kVDim + 4 * lane;
+      float inv32 = inv;
+      asm volatile("" : "+v"(inv32));
+      float* po = reinterpret_cast<float*>(p.part_o) + prow0 * kVDim + 4 * e_lane;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if ((f32_rows >> (16 * half)) & 0xffffu) {
-          if ((l32 >> 4) == half) {
+          if ((e_l32 >> 4) == half) {
 #pragma unroll
             for (int db = 0; db < 16; ++db)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 f32x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv;
-                *reinterpret_cast<f32x4*>(stage + (l32 & 15) * kStride32 + 4 * (32 * db + 8 * q + 4 * g)) = v;
+                for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * q + e] * inv32;
+                *reinterpret_cast<f32x4*>(stage + (e_l32 & 15) * kStride32 + 4 * (32 * db + 8 * q + 4 * e_g)) = v;
               }
           }
           asm volatile("" ::: "memory");  // the reads below see every lane's writes
@@ -1074,33 +1134,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
             if ((f32_rows >> (16 * half + r)) & 1) {
 #pragma unroll
               for (int c = 0; c < 2; ++c) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride32 + 1024 * c + 16 * lane);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride32 + 1024 * c + 16 * e_lane);
                 store_through(po + (size_t)(16 * half + r) * kVDim + 256 * c, v);
               }
             }
           }
           asm volatile("" ::: "memory");  // read before the next half overwrites the region
         }
-      }
-    }
-    // fp16 rows: the whole wavefront's 32 rows at once
-    {
-#pragma unroll
-      for (int db = 0; db < 16; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[db][4 * q + e] * inv);
-          *reinterpret_cast<f16x4*>(stage + l32 * kStride + 2 * (32 * db + 8 * q + 4 * g)) = v;
-        }
-      asm volatile("" ::: "memory");  // the reads below see every lane's writes
-      const uint64_t half_rows = __ballot(as_half && g == 0);  // bit r: row l32 = r
-      _Float16* po = reinterpret_cast<_Float16*>(p.part_o) + prow0 * (2 * kVDim) + 8 * lane;
-#pragma unroll 4
-      for (int r = 0; r < kRowsPerWave; ++r) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * kStride + 16 * lane);
-        if ((half_rows >> r) & 1) store_through(po + (size_t)r * (2 * kVDim), v);
       }
     }
   }

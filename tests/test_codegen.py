@@ -175,3 +175,33 @@ def test_tile_loops_touch_no_scratch(asm):
         bad = [code[k] for k in range(a, b + 1) if code[k].startswith("scratch_") or
                (code[k].startswith("buffer_") and "s[0:3]" in code[k])]
         assert not bad, f"tile loop at lines {a + 1}-{b + 1} touches scratch: {bad[:3]}"
+
+
+def _kernel_metadata(asm):
+    """Per kernel (mangled name): its private segment bytes and VGPR spills."""
+    text = "\n".join(asm)
+    out = {}
+    for block in re.split(r"\n\s*- \.", text)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        seg = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        if name and seg:
+            spills = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
+            out[name.group(1)] = (int(seg.group(1)), int(spills.group(1)) if spills else 0)
+    return out
+
+
+def test_scratch_stays_small(asm):
+    """The partial kernel's walk fills the register file (the query fragments,
+    the scores, P and the K/V reads in flight in VGPRs, the output accumulators
+    in every AGPR), so whatever is live across it costs scratch.  The unit
+    set-up and the epilogue recompute their lane values, keep the plan in
+    scalar registers and read each accumulator once on the common path: a few
+    words per lane remain, and the other kernels use none."""
+    meta = _kernel_metadata(asm)
+    partial = {k: v for k, v in meta.items() if "partial_kernel" in k}
+    assert len(partial) == 4, sorted(meta)
+    for k, (seg, spills) in partial.items():
+        assert seg <= 16 and spills <= 4, f"{k}: {seg} bytes of scratch, {spills} VGPR spills"
+    for k, (seg, spills) in meta.items():
+        if "partial_kernel" not in k:
+            assert seg == 0 and spills == 0, f"{k}: {seg} bytes of scratch"
