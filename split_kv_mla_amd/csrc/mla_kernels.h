@@ -238,7 +238,8 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
       const int T = __builtin_amdgcn_readlane(cinc, 63);
       const int wmin = max(1, ceil_div(T, p.slots));
       const int m = ceil_div(wmin, p.tpi_max);
-      const int U = ceil_div(wmin, m);
+      // cells of U tiles, no shorter than min_item_tiles where the window allows
+      const int U = min(max(ceil_div(wmin, m), min_item_tiles(p.rows_total)), p.tpi_max);
       const int cex = cinc - cost;
       const int items = pair_items(cex + kPieceCost, t, U);
       const int iinc = wave_incl_scan(items);
@@ -279,7 +280,7 @@ __device__ Plan make_plan(const DecodeParams& p, int* starts, int* cstart, int* 
   }
   const int wmin = max(1, ceil_div(T, p.slots));
   const int m = ceil_div(wmin, p.tpi_max);
-  const int U = ceil_div(wmin, m);
+  const int U = min(max(ceil_div(wmin, m), min_item_tiles(p.rows_total)), p.tpi_max);
   const bool keep = P <= kPlanPairsLds;
   int crun = 0, irun = 0;
   if (keep || publish) {
@@ -444,15 +445,16 @@ __device__ __forceinline__ void mfma_vgpr_next_valu(f32x16& s, const bf16x8& a, 
 }
 __device__ __forceinline__ void mfma_vgpr_done(f32x16& s) { asm volatile("s_nop 11" : "+v"(s)); }
 
-// 16 bytes per lane stored with system-scope coherence (sc0 sc1): written
-// through to memory rather than left dirty in this XCD's L2, so the end of
-// the kernel has less to write back before the combine may start.  Used for
-// the whole 1 KiB partial rows.  The two wait states after the store cover
+// 16 bytes per lane stored with device-scope coherence (sc1): written through
+// to memory rather than left dirty in this XCD's L2, so the end of the kernel
+// has less to write back before the combine may start (the kernel boundary,
+// not these bits, is what makes the rows visible to it).  Used for the whole
+// 1 KiB partial rows.  The two wait states after the store cover
 // the VMEM store-data hazard: the compiler does not see an assembly store,
 // and a store of more than 8 bytes reads its data registers after issue, so
 // the very next VALU instruction must not overwrite them.
 __device__ __forceinline__ void store_through(void* ptr, const f32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(ptr), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(ptr), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {

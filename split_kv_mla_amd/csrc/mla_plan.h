@@ -84,6 +84,17 @@ MLA_HD int32_t pair_items(int32_t x0, int32_t tiles, int32_t U) {
   return tiles > 0 ? (x0 + tiles - 1) / U - x0 / U + 1 : 0;
 }
 
+// Shortest item, in tiles, whose partial (its row group's rows, 1 KiB each as
+// fp16) is at most the cache bytes it reads (1152 per token): shorter items
+// spend more of a launch writing partials, and merging them, than reading the
+// cache.  A row group holds at most 4 * kRowsPerWave rows.
+MLA_HD int32_t min_item_tiles(int32_t rows_total) {
+  const int32_t r = rows_total < 4 * kRowsPerWave ? rows_total : 4 * kRowsPerWave;
+  const int32_t per_tile = kTile * kHeadDim * 2;
+  const int32_t t = (r * 1024 + per_tile - 1) / per_tile;
+  return t > 1 ? t : 1;
+}
+
 // Workgroup slots per row group: slot j of every row group runs on XCD j % 8
 // (workgroup i runs on XCD i % 8), so the row groups of one slot share the
 // KV tiles they read through that XCD's L2.

@@ -79,15 +79,23 @@ def _tpi_max(S, I, bs):
     return t
 
 
-def _even_split(tiles, slots, tpi_max):
+def _min_item_tiles(rows_total):
+    """Shortest item of the device plan: its partial (rows of its row group,
+    1 KiB each) no larger than the cache bytes it reads (32 x 1152 per tile)."""
+    r = min(rows_total, 128)
+    return max(1, -(-(r * 1024) // (32 * 1152)))
+
+
+def _even_split(tiles, slots, tpi_max, rows_total=1):
     """Model of the device plan: pairs end to end on a cost axis (PIECE_COST +
-    tiles each), cut into `slots` equal ranges of m cells of U units.
+    tiles each), cut into `slots` equal ranges of m cells of U units, U no
+    shorter than _min_item_tiles(rows_total) where tpi_max allows.
     Returns (U, W, T, pieces) with pieces = (slot, pair, item, tile0, tile1)."""
     costs = [t + PIECE_COST if t > 0 else 0 for t in tiles]
     T = sum(costs)
     wmin = max(1, -(-T // slots))
     m = -(-wmin // tpi_max)
-    U = -(-wmin // m)
+    U = min(max(-(-wmin // m), _min_item_tiles(rows_total)), tpi_max)
     W = m * U
     cst, ist, c, i = [], [], 0, 0
     for t, k in zip(tiles, costs):
@@ -118,8 +126,9 @@ def test_even_split_covers_every_tile_once_with_balanced_slots():
         P = rng.choice([1, 3, 8, 64, 200])
         tiles = [rng.choice([0, 1, 2, 7, 33, 469, 2000, rng.randrange(1, 5000)]) for _ in range(P)]
         slots = rng.choice([256, 128, 80, 64, 32])
-        tpi_max = rng.choice([7, 64, 512, 4000])
-        U, W, T, pieces = _even_split(tiles, slots, tpi_max)
+        tpi_max = rng.choice([2, 7, 64, 512, 4000])
+        rows = rng.choice([1, 16, 128, 512])
+        U, W, T, pieces = _even_split(tiles, slots, tpi_max, rows)
         seen = {}
         for slot, pr, item, t0, t1 in pieces:
             assert 0 <= t0 < t1 <= tiles[pr] and t1 - t0 <= U <= tpi_max
@@ -145,8 +154,25 @@ def _plan_items_when_full(B, R, S, I, bs, maxb):
     slots = 8 * (32 // groups)
     L = maxb * bs
     tiles = [(((L // (S * I)) * I + min(I, max(0, L % (S * I) - s * I))) + 31) // 32 for s in range(S)] * B
-    U, W, T, pieces = _even_split(tiles, slots, _tpi_max(S, I, bs))
+    U, W, T, pieces = _even_split(tiles, slots, _tpi_max(S, I, bs), R * 128)
     return len(pieces), cap
+
+
+def test_items_are_not_shorter_than_their_partial():
+    """With 128 query rows a piece of fewer than 4 tiles would write more
+    partial bytes (128 KiB) than it reads from the cache (36 KiB per tile):
+    the plan keeps items at least that long, unless the table window forbids
+    it.  One shard of the 120000-token request (469 tiles over 256 slots):
+    118 items of 4 tiles, partial bytes 0.90 of the shard's cache bytes."""
+    assert [_min_item_tiles(r) for r in (1, 16, 36, 37, 128, 512)] == [1, 1, 1, 2, 4, 4]
+    U, W, T, pieces = _even_split([469], 256, 511, 128)
+    assert U == 4 and len(pieces) == 118
+    assert len(pieces) * 128 * 1024 <= 15000 * 1152
+    # cells are aligned on the cost axis: only a pair's first and last items are shorter
+    assert all(t1 - t0 == 4 for _, _, _, t0, t1 in pieces[1:-1])
+    # a window of 2 tiles caps U below the minimum
+    U, W, T, pieces = _even_split([469], 256, 2, 128)
+    assert U == 2
 
 
 def test_plan_capacity_covers_longest_requests():
