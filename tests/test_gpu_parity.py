@@ -2,8 +2,9 @@
 
 Tolerances: output |err| <= 2e-3 + 1e-2 |ref| elementwise; LSE |err| <= 1e-3;
 the -inf pattern of the per-shard LSE and the +0.0 output of empty rows are
-bit-exact.  Small cases compare every element; the full-size workloads compare
-sampled (request, head) rows that the oracle computes one by one.
+bit-exact.  Small cases and the five standard workloads at full size compare
+every element of out, lse[S, B, R, H] and lse_final; the two full-block-table
+capacity cases compare every request and row of sampled heads.
 """
 
 import math
