@@ -77,6 +77,10 @@ SMALL = [
     ("rows_512", [200], 4, 128, 2, 1, 64),
     ("rows_1024_max", [150, 40], 8, 128, 4, 1, 64),
     ("bs1024_i5", [2500], 1, 32, 3, 5, 1024),
+    # one request whose block-table row (3000 entries) is wider than the LDS
+    # table: its query rows are copied before the plan, each item's window
+    # after them
+    ("b1_table_past_lds", [3000], 1, 16, 3, 1, 1),
 ]
 
 
