@@ -917,6 +917,79 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
         }
       };
 
+      // Value products kPhase1 .. 63 of a tile with the next tile's softmax
+      // (scores sc of item tile kt -> P against the fixed reference msafe)
+      // cut into pieces between them: the wavefront issues in order, so VALU
+      // work left in one block would hold the matrix pipe idle while it
+      // issues.  Each product and the pieces after it form one scheduling
+      // region (sched_barrier), and the pieces' inputs and outputs are pinned
+      // there (empty asm), so that no pass moves them out.  The arithmetic,
+      // and the order of the denominator's sum, are those of prep and make_p.
+      constexpr int kPhase1 = 28;
+      auto p_under_pv = [&](PFrag& pn, f32x16& sc, const f32x16& ks, int kt, float msafe, auto& pv_step) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const int jt = (t0 + kt) * kTile + 4 * g;
+        asm volatile("" : "+v"(msafe));
+        float xs[16];
+        uint32_t hw[8], lw[8];
+        // pieces: 0-7 scale (fp8) and mask two scores each; then three per
+        // score pair r: the exponentials of scores 2r and 2r+1, then their
+        // bf16 hi and lo halves
+        auto piece = [&](int q) {
+          if (q < 8) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int i = 2 * q + e;
+              float v = sc[i];
+              asm volatile("" : "+v"(v));
+              if constexpr (kFp8) v *= ks[i];
+              v = (jt + 8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : v;
+              asm volatile("" : "+v"(v));
+              sc[i] = v;
+            }
+          } else {
+            const int r = (q - 8) / 3, w = (q - 8) % 3;
+            if (w < 2) {
+              const int j = 2 * r + w;
+              float v = sc[j];
+              asm volatile("" : "+v"(v));
+              float x = __builtin_amdgcn_exp2f(fmaf(v, c, -msafe));
+              l_run += x;
+              if constexpr (kFp8) x *= ks[j];
+              xs[j] = x;
+              asm volatile("" : "+v"(xs[j]), "+v"(l_run));
+            } else {
+              const bf16x2 h2 = {(__bf16)xs[2 * r], (__bf16)xs[2 * r + 1]};
+              hw[r] = __builtin_bit_cast(uint32_t, h2);
+              if constexpr (kLo) {
+                const float f0 = __builtin_bit_cast(float, hw[r] << 16);
+                const float f1 = __builtin_bit_cast(float, hw[r] & 0xffff0000u);
+                const bf16x2 l2 = {(__bf16)(xs[2 * r] - f0), (__bf16)(xs[2 * r + 1] - f1)};
+                lw[r] = __builtin_bit_cast(uint32_t, l2);
+                asm volatile("" : "+v"(lw[r]));
+              }
+              asm volatile("" : "+v"(hw[r]));
+            }
+          }
+        };
+        constexpr int kPieces = 32;
+        constexpr int kN2 = 64 - kPhase1;
+#pragma unroll
+        for (int i = 0; i < kN2; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+          pv_step(kPhase1 + i);
+#pragma unroll
+          for (int q = (i * kPieces + kN2 - 1) / kN2; q < ((i + 1) * kPieces + kN2 - 1) / kN2; ++q) piece(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          pn.hi[kb] = __builtin_bit_cast(bf16x8, u32x4{hw[4 * kb], hw[4 * kb + 1], hw[4 * kb + 2], hw[4 * kb + 3]});
+          if constexpr (kLo)
+            pn.lo[kb] = __builtin_bit_cast(bf16x8, u32x4{lw[4 * kb], lw[4 * kb + 1], lw[4 * kb + 2], lw[4 * kb + 3]});
+        }
+      };
+
       if constexpr (kMaxOnly) {
         for (int k = 0; k < nt; ++k) {
           // tile k resident: the prologue always fills kStages-1 stages, so the
@@ -953,6 +1026,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           make_p(pf, sc, msafe, 0, ks);
           make_p(pf, sc, msafe, 1, ks);
         }
+        // The reference of every row is fixed by now: a row's tokens in the
+        // item are a prefix of its tiles, so a row either has a token in the
+        // first tile or none in the item (and no score that is not masked).
+        // The walk below masks the scores but never takes their maximum.
+        float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
         for (int k = 0; k < nt; ++k) {
           const bool more = k + 1 < nt;
           if (more) {
@@ -982,8 +1060,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
           };
           {
             // the next tile's 36 score products alternate with this tile's
-            // first 36 PV products; K reads run kAhead products ahead.  In the
-            // last iteration the next stage holds no tile of the item: every
+            // first kPhase1 PV products; K reads run kAhead products ahead.  In
+            // the last iteration the next stage holds no tile of the item: every
             // score there is masked, so its P is zero and adds nothing.
             constexpr int kAhead = 4;
             f32x16 sc;
@@ -1004,16 +1082,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(DecodeParams p) {
                 else mfma_vgpr_next(sc, kf[i], qf[i]);
               }
               if (i + kAhead < 36) kf[i + kAhead] = k_frag(nbuf, i + kAhead);
-              pv_step(i);
+#pragma unroll
+              for (int j = i * kPhase1 / 36; j < (i + 1) * kPhase1 / 36; ++j) pv_step(j);
             }
             mfma_vgpr_done(sc);
             const f32x16 ks = tile_scales(nbuf);
-            const float msafe = prep(sc, k + 1, ks);
             PFrag pn;
-            make_p(pn, sc, msafe, 0, ks);
-            make_p(pn, sc, msafe, 1, ks);
-#pragma unroll
-            for (int i = 36; i < 64; ++i) pv_step(i);
+            p_under_pv(pn, sc, ks, k + 1, msafe, pv_step);
             pf = pn;
           }
         }

@@ -196,12 +196,13 @@ def test_scratch_stays_small(asm):
     in every AGPR), so whatever is live across it costs scratch.  The unit
     set-up and the epilogue recompute their lane values, keep the plan in
     scalar registers and read each accumulator once on the common path: a few
-    words per lane remain, and the other kernels use none."""
+    words per lane remain (at most five, all outside the tile loops, which the
+    test above checks), and the other kernels use none."""
     meta = _kernel_metadata(asm)
     partial = {k: v for k, v in meta.items() if "partial_kernel" in k}
     assert len(partial) == 4, sorted(meta)
     for k, (seg, spills) in partial.items():
-        assert seg <= 16 and spills <= 4, f"{k}: {seg} bytes of scratch, {spills} VGPR spills"
+        assert seg <= 20 and spills <= 4, f"{k}: {seg} bytes of scratch, {spills} VGPR spills"
     for k, (seg, spills) in meta.items():
         if "partial_kernel" not in k:
             assert seg == 0 and spills == 0, f"{k}: {seg} bytes of scratch"
