@@ -277,6 +277,27 @@ def test_shard_map_against_dealing():
                         assert (j // I) * S * I + s * I + (j % I) == t
 
 
+def test_a_rows_tokens_are_a_prefix_of_every_shard():
+    """The tokens a verification row sees (its causal prefix of the request)
+    are, in every shard, that shard's first local tokens: dealt tokens keep
+    their order inside a shard, so a row's tokens in any run of a shard's
+    local tiles are a prefix of that run.  The partial kernel relies on it:
+    a row with a token in an item has one in the item's first tile, whose
+    maximum is then the row's reference for the whole item."""
+    for S, I in [(1, 1), (2, 1), (8, 1), (8, 16), (3, 5), (16, 64)]:
+        for seq_len in (0, 1, 5, S * I - 1, 3 * S * I + 2, 1000):
+            owner = _brute.deal_tokens(seq_len, S, I)
+            for R in (1, 2, 4):
+                for r in range(R):
+                    for causal in (True, False):
+                        n = oracle.row_length(seq_len, R, r, causal)
+                        for s in range(S):
+                            local = [t for t in range(seq_len) if owner[t] == s]
+                            seen = [j for j, t in enumerate(local) if t < n]
+                            assert seen == list(range(len(seen))), (S, I, seq_len, R, r, causal, s)
+                            assert len(seen) == _local_length(n, S, I, s)
+
+
 def test_padding_row_mask_semantics():
     # requests: lengths 3, 0, 5, 0; query rows 1, 2, 1, 2
     mask = oracle.padding_row_mask([3, 0, 5, 0], [0, 1, 3, 4, 6])
